@@ -1,0 +1,174 @@
+"""fp64 CPU oracle for verification attention — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the package smoke check and the benchmark's CPU-baseline leg
+may import this module.  The product path (the HIP library and its binding)
+never does, and the oracle imports nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, explicit mask rows);
+this file only builds it with gcc and marshals numpy arrays through ctypes.
+The sparse-cache gather (Dustin page, "Verification workflow": a compressed
+cache formed from the selected tokens) is a pure copy and is written here
+with numpy indexing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+PART_PREFIX, PART_TREE = 1, 2
+PART_BOTH = PART_PREFIX | PART_TREE
+
+_lock = threading.Lock()
+_lib = None
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_draft", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_capacity", ctypes.c_int32),
+        ("n_sel", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("parts", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+    ]
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < max(
+            os.path.getmtime(SRC), os.path.getmtime(os.path.join(HERE, "oracle.h"))):
+        tmp = LIB + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(LIB)
+            P = ctypes.c_void_p
+            lib.oracle_ancestor_mask.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P]
+            lib.oracle_ancestor_mask.restype = ctypes.c_int
+            lib.oracle_verify_attn.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, P, P, P,
+                                               ctypes.c_int64, P, P]
+            lib.oracle_verify_attn.restype = ctypes.c_int
+            lib.oracle_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+            lib.oracle_lse_merge.restype = None
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def ancestor_mask(parent: np.ndarray) -> np.ndarray:
+    """uint64 [B, N] ancestor bitmask by walking parent pointers."""
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    if parent.ndim == 1:
+        parent = parent[None]
+    B, N = parent.shape
+    out = np.zeros((B, N), dtype=np.uint64)
+    rc = _load().oracle_ancestor_mask(_ptr(parent), B, N, _ptr(out))
+    if rc != 0:
+        raise ValueError("invalid parent array")
+    return out
+
+
+def verify_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_lens: np.ndarray,
+                parent: Optional[np.ndarray] = None, anc_mask: Optional[np.ndarray] = None,
+                kv_idx: Optional[np.ndarray] = None, *, bf16: bool,
+                scale: Optional[float] = None, parts: int = PART_BOTH,
+                rows: Optional[Sequence[Tuple[int, int, int]]] = None
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 verification attention.
+
+    q ``[B, N, Hq, D]``; k, v ``[B, Hkv, S_cap, D]`` (float32, or uint16 bf16
+    bits when ``bf16``); ctx_lens ``[B]``; one of parent / anc_mask ``[B, N]``;
+    kv_idx ``[B, Hkv, n_sel]`` for the sparse prefix.  Returns (o, lse):
+    ``[B, N, Hq, D]`` / ``[B, N, Hq]`` for all rows, or ``[R, D]`` / ``[R]``
+    for the (b, i, h) triples in ``rows``.
+    """
+    B, N, Hq, D = q.shape
+    Bk, Hkv, cap, Dk = k.shape
+    if (Bk, Dk) != (B, D) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    want = np.uint16 if bf16 else np.float32
+    q = np.ascontiguousarray(q, dtype=want)
+    k = np.ascontiguousarray(k, dtype=want)
+    v = np.ascontiguousarray(v, dtype=want)
+    ctx_lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    if parent is not None:
+        parent = np.ascontiguousarray(parent, dtype=np.int32).reshape(B, N)
+    if anc_mask is not None:
+        anc_mask = np.ascontiguousarray(anc_mask, dtype=np.uint64).reshape(B, N)
+    n_sel = 0
+    if kv_idx is not None:
+        kv_idx = np.ascontiguousarray(kv_idx, dtype=np.int32)
+        n_sel = kv_idx.shape[-1]
+        if kv_idx.shape != (B, Hkv, n_sel) or n_sel == 0:
+            raise ValueError("kv_idx must be [B, Hkv, n_sel] with n_sel > 0")
+    d = _Desc(B, N, Hq, Hkv, D, cap, n_sel, BF16 if bf16 else F32, parts,
+              float(scale) if scale is not None else 1.0 / float(np.sqrt(D)))
+    if rows is None:
+        rows_arr = None
+        o = np.zeros((B, N, Hq, D), dtype=np.float64)
+        lse = np.zeros((B, N, Hq), dtype=np.float64)
+        n_rows = 0
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+        n_rows = rows_arr.shape[0]
+        o = np.zeros((n_rows, D), dtype=np.float64)
+        lse = np.zeros((n_rows,), dtype=np.float64)
+    rc = _load().oracle_verify_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(ctx_lens),
+                                    _ptr(parent), _ptr(anc_mask), _ptr(kv_idx), _ptr(rows_arr),
+                                    n_rows, _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_verify_attn rejected its arguments")
+    return o, lse
+
+
+def lse_merge(lse_parts: np.ndarray, o_parts: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Merge P partial (o, lse) results of one row: lse_parts [P], o_parts [P, D]."""
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64).reshape(-1)
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    P, D = o_parts.shape
+    assert lse_parts.shape == (P,)
+    o = np.zeros(D, dtype=np.float64)
+    lse = np.zeros(1, dtype=np.float64)
+    _load().oracle_lse_merge(P, D, _ptr(lse_parts), _ptr(o_parts), _ptr(o), _ptr(lse))
+    return o, float(lse[0])
+
+
+def gather_kv(k: np.ndarray, v: np.ndarray, kv_idx: np.ndarray):
+    """Compressed cache: K_sel[b, g, s] = K[b, g, kv_idx[b, g, s]] (and V)."""
+    B, Hkv, n_sel = kv_idx.shape
+    bi = np.arange(B)[:, None, None]
+    gi = np.arange(Hkv)[None, :, None]
+    return k[bi, gi, kv_idx], v[bi, gi, kv_idx]

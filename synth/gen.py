@@ -1,0 +1,322 @@
+"""Seeded generators for verification-attention workloads.
+
+Nothing here computes attention.  The generators only draw numbers with a
+``numpy.random.Generator(PCG64(seed))`` in a fixed order and lay them out in
+the layouts the C ABI takes:
+
+* ``q``        ``[B, N, Hq, D]``
+* ``k``, ``v`` ``[B, Hkv, S_cap, D]``; the draft block's K/V sit at cache
+  positions ``[ctx_b, ctx_b + N)``; slots at ``ctx_b + N`` and beyond are NaN.
+* ``ctx_lens`` ``int32 [B]``
+* ``parent``   ``int32 [B, N]`` with ``parent[i]`` in ``[-1, i-1]``; -1 is the
+  cached prefix (the tree root).
+* ``kv_idx``   ``int32 [B, Hkv, n_sel]`` sorted and unique (sparse workloads).
+
+Floating values are drawn in fp32 and, for bf16 workloads, rounded to bf16
+with round-to-nearest-even; bf16 tensors are carried as their ``uint16`` bit
+patterns so that the oracle and the GPU see exactly the same numbers.
+
+Draw order (fixed): ctx_lens -> parents -> index sets -> Q -> K -> V.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+# ----------------------------------------------------------------------------
+# bf16 bit handling (input preparation, not method arithmetic)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); return bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    out = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to the fp32 values they denote (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# draft-tree shapes
+# ----------------------------------------------------------------------------
+
+def uniform_parents(rng: np.random.Generator, n: int) -> np.ndarray:
+    """parent[i] uniform in [-1, i-1] (the tiny tree workload's recipe)."""
+    return np.array([rng.integers(-1, i) for i in range(n)], dtype=np.int32)
+
+
+def chain_parents(n: int) -> np.ndarray:
+    """A linear draft block: node i's parent is i-1 (causal inside the block)."""
+    return np.arange(-1, n - 1, dtype=np.int32)
+
+
+def random_tree_parents(rng: np.random.Generator, n: int, max_depth: int,
+                        max_branch: int = 4) -> np.ndarray:
+    """Seeded draft tree with bounded depth and branching.
+
+    Node i picks its parent uniformly among the prefix root (-1) and the earlier
+    nodes j < i whose depth is below ``max_depth`` and that have fewer than
+    ``max_branch`` children.  The prefix root counts for branching too; its
+    children have depth 1.
+    """
+    parent = np.empty(n, dtype=np.int32)
+    depth = np.zeros(n, dtype=np.int64)
+    children = np.zeros(n, dtype=np.int64)
+    root_children = 0
+    for i in range(n):
+        eligible = []
+        if root_children < max_branch:
+            eligible.append(-1)
+        for j in range(i):
+            if depth[j] < max_depth and children[j] < max_branch:
+                eligible.append(j)
+        if not eligible:
+            raise ValueError("tree capacity exhausted: raise max_depth or max_branch")
+        p = eligible[int(rng.integers(0, len(eligible)))]
+        parent[i] = p
+        if p < 0:
+            root_children += 1
+            depth[i] = 1
+        else:
+            children[p] += 1
+            depth[i] = depth[p] + 1
+    return parent
+
+
+def zipf_ranked_draw(rng: np.random.Generator, m: int, n_draw: int, zipf_a: float):
+    """Draw ``n_draw`` of ``m`` positions without replacement, P ~ rank**-a.
+
+    Each position gets a random rank (a permutation of 1..m); the draw is a
+    Gumbel-top-k over log-weights.  Returns (positions, their ranks).
+    """
+    rank = rng.permutation(m).astype(np.float64) + 1.0
+    u = rng.random(m)
+    key = -zipf_a * np.log(rank) - np.log(-np.log(np.maximum(u, 1e-300)))
+    if n_draw:
+        pick = np.argpartition(-key, n_draw - 1)[:n_draw]
+    else:
+        pick = np.empty(0, dtype=np.int64)
+    return pick, rank[pick]
+
+
+def zipf_index_set(rng: np.random.Generator, ctx: int, n_sel: int, n_sink: int,
+                   n_recent: int, zipf_a: float) -> np.ndarray:
+    """Sorted unique index set: sinks + recent window + Zipf-ranked fill.
+
+    The middle positions ``[n_sink, ctx - n_recent)`` get a seeded random rank
+    r (a permutation of 1..M); ``n_sel - n_sink - n_recent`` of them are drawn
+    without replacement with probability proportional to ``r ** -zipf_a``
+    (Gumbel-top-k).  The set mimics the Dustin page's fixed-size verification
+    set (sink prefix, recent window, ranked fill).
+    """
+    n_fill = n_sel - n_sink - n_recent
+    mid_lo, mid_hi = n_sink, ctx - n_recent
+    m = mid_hi - mid_lo
+    if n_fill < 0 or n_fill > m:
+        raise ValueError("index-set budget does not fit the context")
+    pick, _ = zipf_ranked_draw(rng, m, n_fill, zipf_a)
+    idx = np.concatenate([np.arange(0, n_sink), pick + mid_lo, np.arange(mid_hi, ctx)])
+    idx = np.sort(idx).astype(np.int32)
+    assert idx.size == n_sel and np.unique(idx).size == n_sel
+    return idx
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_draft: int
+    ctx: Tuple[int, int]          # ctx_b drawn uniformly in [lo, hi]; lo == hi: fixed
+    dtype: str                    # "f32" or "bf16"
+    tree: str                     # "uniform", "tree" or "chain"
+    max_depth: int = 0
+    max_branch: int = 4
+    q_scale: float = 1.0
+    kv_scale: float = 1.0
+    sink_rows: int = 0            # first rows of K and V scaled by sink_scale
+    sink_scale: float = 1.0
+    n_sel: int = 0                # > 0: sparse workload with an index set per (b, kv head)
+    n_sink: int = 4
+    n_recent: int = 512
+    zipf_a: float = 1.1
+    description: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def kv_capacity(self) -> int:
+        return self.ctx[1] + self.n_draft
+
+    @property
+    def sparse(self) -> bool:
+        return self.n_sel > 0
+
+    def scaled(self, **kw) -> "Workload":
+        """Same recipe with some fields replaced (smaller parity cases)."""
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_tree": Workload(
+        name="tiny_tree", seed=1, batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64,
+        n_draft=8, ctx=(256, 256), dtype="f32", tree="uniform",
+        description="batch 1, 1/1 heads, D64, fp32, 256-token prefix, 8-node uniform tree"),
+    "tree32k": Workload(
+        name="tree32k", seed=2, batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        n_draft=64, ctx=(32768, 32768), dtype="bf16", tree="tree", max_depth=6,
+        q_scale=1.0, kv_scale=0.5,
+        description="batch 1, 32/8 heads, D128, bf16, 32768-token context, 64-node tree"),
+    "chain_b16": Workload(
+        name="chain_b16", seed=3, batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        n_draft=8, ctx=(16384, 32768), dtype="bf16", tree="chain",
+        q_scale=0.5, kv_scale=0.5,
+        description="batch 16, 32/8 heads, D128, bf16, contexts in [16384, 32768], 8-token chain"),
+    "tree128k": Workload(
+        name="tree128k", seed=4, batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        n_draft=64, ctx=(131072, 131072), dtype="bf16", tree="tree", max_depth=8,
+        q_scale=1.0, kv_scale=0.5, sink_rows=4, sink_scale=8.0,
+        description="batch 1, 32/8 heads, D128, bf16, 131072-token context, 64-node tree, x8 sinks"),
+    "sparse64k": Workload(
+        name="sparse64k", seed=5, batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        n_draft=8, ctx=(65536, 65536), dtype="bf16", tree="chain",
+        q_scale=0.5, kv_scale=0.5, n_sel=4096, n_sink=4, n_recent=512, zipf_a=1.1,
+        description="batch 8, 32/8 heads, D128, bf16, 65536-token context, 4096-entry index sets"),
+}
+
+
+@dataclass
+class VerifyInputs:
+    wl: Workload
+    q: np.ndarray                  # f32, or uint16 bf16 bits
+    k: np.ndarray
+    v: np.ndarray
+    ctx_lens: np.ndarray           # int32 [B]
+    parent: np.ndarray             # int32 [B, N]
+    kv_idx: Optional[np.ndarray] = None   # int32 [B, Hkv, n_sel]
+    meta: Dict[str, str] = field(default_factory=dict)
+
+    @property
+    def is_bf16(self) -> bool:
+        return self.wl.dtype == "bf16"
+
+    def manifest(self) -> Dict[str, str]:
+        """SHA-256 of every tensor (reproducibility check across machines)."""
+        out = {}
+        for name in ("q", "k", "v", "ctx_lens", "parent", "kv_idx"):
+            a = getattr(self, name)
+            if a is not None:
+                out[name] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+        return out
+
+
+def _normal(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return x
+
+
+def _encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+
+
+def make_inputs(wl, seed: Optional[int] = None, poison_unselected: bool = False,
+                **overrides) -> VerifyInputs:
+    """Draw one workload.  ``wl`` is a Workload or a key of ``WORKLOADS``.
+
+    ``overrides`` replace Workload fields (e.g. ``ctx=(1000, 1000)`` for a
+    smaller parity case with the same recipe).  ``poison_unselected`` writes
+    NaN into every prefix row a sparse index set leaves out, so that a kernel
+    that reads an unselected row cannot pass a parity test.
+    """
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    if overrides:
+        wl = wl.scaled(**overrides)
+    if seed is None:
+        seed = wl.seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, N, Hq, Hkv, D = wl.batch, wl.n_draft, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    if Hq % Hkv:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    s_cap = wl.kv_capacity
+
+    # 1. context lengths
+    lo, hi = wl.ctx
+    if lo == hi:
+        ctx = np.full(B, lo, dtype=np.int32)
+    else:
+        ctx = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+
+    # 2. parents
+    parent = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        if wl.tree == "chain":
+            parent[b] = chain_parents(N)
+        elif wl.tree == "uniform":
+            parent[b] = uniform_parents(rng, N)
+        elif wl.tree == "tree":
+            parent[b] = random_tree_parents(rng, N, wl.max_depth, wl.max_branch)
+        else:
+            raise ValueError(f"unknown tree shape {wl.tree!r}")
+
+    # 3. index sets
+    kv_idx = None
+    if wl.sparse:
+        kv_idx = np.empty((B, Hkv, wl.n_sel), dtype=np.int32)
+        for b in range(B):
+            for g in range(Hkv):
+                kv_idx[b, g] = zipf_index_set(rng, int(ctx[b]), wl.n_sel, wl.n_sink,
+                                              wl.n_recent, wl.zipf_a)
+
+    # 4. Q
+    q = _encode(_normal(rng, (B, N, Hq, D), wl.q_scale), wl.dtype)
+
+    # 5./6. K then V, one batch entry at a time to bound host memory
+    caches = []
+    for _ in range(2):
+        dt = np.uint16 if wl.dtype == "bf16" else np.float32
+        cache = np.empty((B, Hkv, s_cap, D), dtype=dt)
+        for b in range(B):
+            x = _normal(rng, (Hkv, s_cap, D), wl.kv_scale)
+            if wl.sink_rows:
+                x[:, :wl.sink_rows, :] *= np.float32(wl.sink_scale)
+            x[:, int(ctx[b]) + N:, :] = np.nan
+            if poison_unselected and kv_idx is not None:
+                keep = np.zeros((Hkv, s_cap), dtype=bool)
+                for g in range(Hkv):
+                    keep[g, kv_idx[b, g]] = True
+                keep[:, int(ctx[b]):] = True
+                x[~keep] = np.nan
+            cache[b] = _encode(x, wl.dtype)
+        caches.append(cache)
+    k, v = caches
+    return VerifyInputs(wl=wl, q=q, k=k, v=v, ctx_lens=ctx, parent=parent, kv_idx=kv_idx,
+                        meta={"seed": str(seed), "workload": wl.name})
