@@ -1,0 +1,189 @@
+/*
+ * hsv — verification attention for speculative decoding on MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a device pointer unless stated
+ * otherwise; every buffer belongs to the caller.  The library allocates and
+ * frees no device memory: scratch lives in the caller's workspace, sized by
+ * hsv_verify_workspace_bytes().  Work is enqueued on `stream` and the calls
+ * return without synchronising the host (except under HSV_FLAG_VALIDATE).
+ * The library keeps no mutable global state, so concurrent calls on different
+ * streams with different workspaces are safe.
+ *
+ * What is computed.  LongSpec ("Long-Context Lossless Speculative Decoding
+ * with Efficient Drafting and Verification"), section 2.C "Hybrid Tree
+ * Attention": the target model verifies a tree of draft tokens; attention is
+ * divided into a cache part (the long history, no mask) and a speculative
+ * part (the draft tokens, under a mask that follows the branches of the
+ * tree), and the two parts' outputs are combined exactly through their
+ * log-sum-exp.  The combined result is therefore plain masked softmax
+ * attention:
+ *
+ *   for sequence b, draft node i, query head h, KV head g = h / (Hq / Hkv):
+ *     A(b,i,g) = P(b,g)  u  { c_b + j : node j is node i or an ancestor of i }
+ *     P(b,g)   = [0, c_b)                       (hsv_verify_attn)
+ *              = { kv_idx[b,g,s] : s < n_sel }  (hsv_verify_attn_sparse)
+ *     s_t  = scale * <q[b,i,h,:], k[b,g,t,:]>
+ *     lse  = log sum_{t in A} exp(s_t)          (natural log)
+ *     o    = sum_{t in A} exp(s_t - lse) * v[b,g,t,:]
+ *
+ * The sparse form follows the Dustin page ("Verification workflow" and
+ * "Limitations"): the target verifies against a compressed cache made of a
+ * selected token subset while the full history stays in place and indexed.
+ *
+ * Conventions (fixed here; the pages leave them open):
+ *   - the draft block's K and V sit in the same cache at positions
+ *     [c_b, c_b + N), node j at c_b + j;
+ *   - node i sees itself and its ancestors (parent chain), never siblings or
+ *     descendants; parent[i] in [-1, i-1], -1 meaning the cached prefix;
+ *   - query head h uses KV head h / (Hq / Hkv) (contiguous groups);
+ *   - an empty key set gives o = 0, lse = -inf (cannot happen when the tree
+ *     part is on: a node always sees itself).
+ *
+ * Layouts (row-major, innermost last, no padding):
+ *   q        [B, N, Hq, D]       in_dtype
+ *   k, v     [B, Hkv, S_cap, D]  in_dtype
+ *   ctx_lens [B]                 int32
+ *   parent   [B, N]              int32
+ *   anc_mask [B, N]              uint64, bit j = node j visible from node i
+ *   kv_idx   [B, Hkv, n_sel]     int32, strictly increasing, each < c_b
+ *   o        [B, N, Hq, D]       out_dtype
+ *   lse      [B, N, Hq]          float
+ *
+ * Errors.  Calls return a status and never print.  Argument checks that need
+ * no device data run first and return before anything is enqueued.  Data
+ * preconditions held in device memory (parent range, ctx_lens bounds, index
+ * order and range) are the caller's contract; with HSV_FLAG_VALIDATE a check
+ * kernel runs first and the call synchronises `stream` to report
+ * HSV_ERR_DEVICE_CHECK.  HIP launch failures return HSV_ERR_HIP.
+ */
+#ifndef HSV_H
+#define HSV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSV_VERSION 1
+
+typedef enum hsv_status {
+  HSV_OK = 0,
+  HSV_ERR_NULL = 1,         /* a required pointer is NULL                        */
+  HSV_ERR_SHAPE = 2,        /* sizes out of range or inconsistent                */
+  HSV_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement       */
+  HSV_ERR_WORKSPACE = 4,    /* workspace missing, too small or misaligned        */
+  HSV_ERR_DEVICE_CHECK = 5, /* HSV_FLAG_VALIDATE found bad device-side data      */
+  HSV_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed        */
+} hsv_status;
+
+typedef enum hsv_dtype { HSV_F32 = 0, HSV_BF16 = 1 } hsv_dtype;
+
+/* Run a device-side check of parent, ctx_lens and kv_idx first; synchronises. */
+#define HSV_FLAG_VALIDATE 1u
+/* Leave out the cache part (prefix) or the speculative part (draft tree).
+ * Each alone is one of the two partial attentions of LongSpec section 2.C. */
+#define HSV_FLAG_NO_PREFIX 2u
+#define HSV_FLAG_NO_TREE 4u
+/* Run one phase only.  A verify call is two phases: PARTIALS (the prefix
+ * splits and the tree part, written to the workspace) and MERGE (the exact
+ * log-sum-exp combination into o and lse).  A MERGE-only call must follow a
+ * PARTIALS-only call with the same descriptor and workspace on the same
+ * stream (or be otherwise ordered after it).  Neither or both bits: both
+ * phases.  Lets a caller time the phases apart or place work between them. */
+#define HSV_FLAG_PHASE_PARTIALS 8u
+#define HSV_FLAG_PHASE_MERGE 16u
+
+typedef struct hsv_verify_desc {
+  int32_t batch;       /* B >= 1                                                */
+  int32_t n_draft;     /* N in [1, 64]                                          */
+  int32_t n_q_heads;   /* Hq >= 1, a multiple of n_kv_heads                     */
+  int32_t n_kv_heads;  /* Hkv >= 1                                              */
+  int32_t head_dim;    /* D: 64 or 128                                          */
+  int32_t kv_capacity; /* S_cap: token slots per (b, kv head) in k and v        */
+  int32_t max_ctx;     /* host-known upper bound on ctx_lens[]; sizes the grid; */
+                       /* max_ctx + N <= S_cap                                  */
+  int32_t n_sel;       /* sparse call: indices per (b, kv head), 1..max_ctx;    */
+                       /* dense call: must be 0                                 */
+  int32_t in_dtype;    /* hsv_dtype of q, k, v                                  */
+  int32_t out_dtype;   /* hsv_dtype of o                                        */
+  float scale;         /* score scale; 0 means 1/sqrt(head_dim)                 */
+  int32_t num_splits;  /* split count over the prefix; 0 = automatic, else 1..256 */
+  uint32_t flags;      /* HSV_FLAG_* bits                                       */
+} hsv_verify_desc;
+
+/* Bytes of workspace hsv_verify_attn / hsv_verify_attn_sparse need for `d`.
+ * Writes *bytes; returns HSV_ERR_SHAPE / HSV_ERR_UNSUPPORTED for a
+ * descriptor the verify calls would reject. */
+hsv_status hsv_verify_workspace_bytes(const hsv_verify_desc *d, size_t *bytes);
+
+/* Dense verification attention: prefix [0, c_b) plus the draft tree.
+ * Give exactly one of `parent` / `anc_mask` (the other NULL); with
+ * HSV_FLAG_NO_TREE both may be NULL.  Writes every element of o and lse.
+ * `workspace` must be 256-byte aligned and at least the reported size;
+ * its contents on entry do not matter. */
+hsv_status hsv_verify_attn(const hsv_verify_desc *d, const void *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *ctx_lens, const int32_t *parent,
+                           const uint64_t *anc_mask, void *o, float *lse,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Sparse verification attention: prefix = the d->n_sel cache positions in
+ * kv_idx[b, g, :] (strictly increasing, each < c_b), plus the draft tree.
+ * Same arguments and rules as hsv_verify_attn otherwise. */
+hsv_status hsv_verify_attn_sparse(const hsv_verify_desc *d, const void *q,
+                                  const void *k_cache, const void *v_cache,
+                                  const int32_t *ctx_lens,
+                                  const int32_t *parent,
+                                  const uint64_t *anc_mask,
+                                  const int32_t *kv_idx, void *o, float *lse,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* Ancestor bitmask of each draft tree (LongSpec section 2.C: the mask of the
+ * speculative part follows the branches of the tree).
+ * parent [B, N] int32 in [-1, i-1]; anc_mask [B, N] uint64 out, bit j set iff
+ * node j is node i or an ancestor of i.  N in [1, 64].  Entries of a
+ * sequence with an out-of-range parent are written as 0. */
+hsv_status hsv_tree_ancestor_mask(const int32_t *parent, uint64_t *anc_mask,
+                                  int32_t batch, int32_t n_draft,
+                                  hipStream_t stream);
+
+/* Compressed cache of the sparse form (Dustin page, "Verification workflow",
+ * step 3): k_out[b,g,s,:] = k_cache[b,g,kv_idx[b,g,s],:], same for v.
+ * k_cache, v_cache [B, Hkv, S_cap, D]; kv_idx [B, Hkv, n_sel] with entries in
+ * [0, S_cap) (an out-of-range entry yields a zero row); k_out, v_out
+ * [B, Hkv, n_sel, D].  A bit-exact copy; dtype is the element type. */
+hsv_status hsv_gather_kv(const void *k_cache, const void *v_cache,
+                         const int32_t *kv_idx, void *k_out, void *v_out,
+                         int32_t batch, int32_t n_kv_heads, int32_t kv_capacity,
+                         int32_t head_dim, int32_t n_sel, int32_t dtype,
+                         hipStream_t stream);
+
+/* Exact log-sum-exp merge of partial attention results (LongSpec section
+ * 2.C: the parts' outputs are combined exactly), e.g. partials over disjoint
+ * key ranges computed on several devices.
+ * o_parts [P, R, D] float, each part normalised within itself;
+ * lse_parts [P, R] float; o [R, D] out_dtype; lse [R] float.
+ *   lse = log sum_p exp(lse_p),  o = sum_p exp(lse_p - lse) * o_p
+ * Parts with lse_p = -inf are skipped (their o_p is never read); a row whose
+ * parts are all -inf gets o = 0, lse = -inf.  P in [1, 1024], D in {64, 128}. */
+hsv_status hsv_lse_merge(const float *o_parts, const float *lse_parts,
+                         int32_t n_parts, int64_t n_rows, int32_t head_dim,
+                         void *o, float *lse, int32_t out_dtype,
+                         hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *hsv_status_string(hsv_status s);
+
+/* HSV_VERSION of the built library. */
+int32_t hsv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSV_H */

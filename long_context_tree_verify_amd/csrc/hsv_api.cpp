@@ -1,0 +1,263 @@
+// C ABI of the verification-attention library: argument checks, the split
+// plan, workspace carving and kernel launches.  No device memory is
+// allocated here; nothing is printed.
+#include <hip/hip_runtime_api.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "hsv.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace hsv {
+
+hipError_t launch_attn_partials_valu(const Plan &p, hipStream_t s);
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxSplits = 256;
+constexpr int kTile = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+hsv_status check_desc(const hsv_verify_desc *d, bool sparse) {
+  if (!d) return HSV_ERR_NULL;
+  if (d->batch < 1 || d->n_draft < 1 || d->n_draft > 64) return HSV_ERR_SHAPE;
+  if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads) return HSV_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return HSV_ERR_UNSUPPORTED;
+  if (d->max_ctx < 0 || d->kv_capacity < 1) return HSV_ERR_SHAPE;
+  if (static_cast<int64_t>(d->max_ctx) + d->n_draft > d->kv_capacity) return HSV_ERR_SHAPE;
+  if (d->in_dtype != HSV_F32 && d->in_dtype != HSV_BF16) return HSV_ERR_UNSUPPORTED;
+  if (d->out_dtype != HSV_F32 && d->out_dtype != HSV_BF16) return HSV_ERR_UNSUPPORTED;
+  if (d->num_splits < 0 || d->num_splits > kMaxSplits) return HSV_ERR_SHAPE;
+  if (!(d->scale >= 0.f) || isinf(d->scale)) return HSV_ERR_SHAPE;
+  const uint32_t known = HSV_FLAG_VALIDATE | HSV_FLAG_NO_PREFIX | HSV_FLAG_NO_TREE |
+                         HSV_FLAG_PHASE_PARTIALS | HSV_FLAG_PHASE_MERGE;
+  if (d->flags & ~known) return HSV_ERR_UNSUPPORTED;
+  if ((d->flags & HSV_FLAG_NO_PREFIX) && (d->flags & HSV_FLAG_NO_TREE)) return HSV_ERR_SHAPE;
+  if (sparse) {
+    if (d->n_sel < 1 || d->n_sel > d->max_ctx) return HSV_ERR_SHAPE;
+  } else if (d->n_sel != 0) {
+    return HSV_ERR_SHAPE;
+  }
+  const int64_t rows = static_cast<int64_t>(d->n_q_heads / d->n_kv_heads) * d->n_draft;
+  if (rows > 4096) return HSV_ERR_UNSUPPORTED;
+  // all flat indices below must fit comfortably in int64; cache slots in int32
+  const int64_t cache_elems =
+      static_cast<int64_t>(d->batch) * d->n_kv_heads * d->kv_capacity * d->head_dim;
+  if (cache_elems / d->head_dim / d->n_kv_heads / d->batch != d->kv_capacity) return HSV_ERR_SHAPE;
+  return HSV_OK;
+}
+
+// Resolve the descriptor into a launch plan (no pointers yet) and the bytes
+// of workspace it needs.
+hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_bytes) {
+  hsv_status st = check_desc(d, sparse);
+  if (st != HSV_OK) return st;
+  *p = Plan{};
+  p->B = d->batch;
+  p->N = d->n_draft;
+  p->Hq = d->n_q_heads;
+  p->Hkv = d->n_kv_heads;
+  p->G = d->n_q_heads / d->n_kv_heads;
+  p->D = d->head_dim;
+  p->R = p->G * p->N;
+  p->cap = d->kv_capacity;
+  p->n_sel = sparse ? d->n_sel : 0;
+  p->max_ctx = d->max_ctx;
+  p->in_dtype = d->in_dtype;
+  p->out_dtype = d->out_dtype;
+  p->scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf(static_cast<float>(d->head_dim));
+  p->scale_log2 = p->scale * 1.4426950408889634f;
+
+  const bool with_prefix = !(d->flags & HSV_FLAG_NO_PREFIX);
+  const bool with_tree = !(d->flags & HSV_FLAG_NO_TREE);
+  const int64_t keys = sparse ? d->n_sel : d->max_ctx;
+  if (with_prefix && keys > 0) {
+    int target;
+    if (d->num_splits > 0) {
+      target = d->num_splits;
+    } else {
+      // Enough (b, kv head, split) work units to cover the GPU twice over,
+      // but no split shorter than four 64-key tiles.
+      const int64_t units = static_cast<int64_t>(p->B) * p->Hkv;
+      const int64_t want = ceil_div(2 * kPlanCUs, units);
+      const int64_t by_len = ceil_div(keys, 4 * kTile);
+      target = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({want, by_len, kMaxSplits})));
+    }
+    p->keys_per_split = static_cast<int32_t>(ceil_div(ceil_div(keys, target), kTile) * kTile);
+    p->n_splits = target;
+  } else {
+    p->n_splits = 0;
+    p->keys_per_split = kTile;
+  }
+  p->tree_part = with_tree ? p->n_splits : -1;
+  p->n_parts = p->n_splits + (with_tree ? 1 : 0);
+
+  const size_t rows = static_cast<size_t>(p->n_parts) * p->B * p->Hkv * p->R;
+  size_t off = 0;
+  off += align_up(rows * p->D * sizeof(float));  // o_part
+  off += align_up(rows * sizeof(float));         // lse_part
+  off += kAlign;                                 // error word
+  *ws_bytes = off;
+  return HSV_OK;
+}
+
+void carve_workspace(Plan *p, void *ws) {
+  char *base = static_cast<char *>(ws);
+  const size_t rows = static_cast<size_t>(p->n_parts) * p->B * p->Hkv * p->R;
+  p->o_part = reinterpret_cast<float *>(base);
+  base += align_up(rows * p->D * sizeof(float));
+  p->lse_part = reinterpret_cast<float *>(base);
+  base += align_up(rows * sizeof(float));
+  p->err = reinterpret_cast<int32_t *>(base);
+}
+
+hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, const void *k,
+                      const void *v, const int32_t *ctx_lens, const int32_t *parent,
+                      const uint64_t *anc, const int32_t *kv_idx, void *o, float *lse, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  if (!d) return HSV_ERR_NULL;
+  Plan p;
+  size_t need = 0;
+  hsv_status st = make_plan(d, sparse, &p, &need);
+  if (st != HSV_OK) return st;
+  const bool with_tree = p.tree_part >= 0;
+  if (!q || !k || !v || !ctx_lens || !o || !lse) return HSV_ERR_NULL;
+  if (sparse && !kv_idx) return HSV_ERR_NULL;
+  if (with_tree && ((parent == nullptr) == (anc == nullptr))) return HSV_ERR_NULL;
+  if (!ws) return HSV_ERR_WORKSPACE;
+  if (ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return HSV_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+       reinterpret_cast<uintptr_t>(v)) % 16)
+    return HSV_ERR_SHAPE;  // 16-byte vector loads
+
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.ctx_lens = ctx_lens;
+  p.parent = with_tree ? parent : nullptr;
+  p.anc = with_tree ? anc : nullptr;
+  p.kv_idx = sparse ? kv_idx : nullptr;
+  p.o = o;
+  p.lse = lse;
+  carve_workspace(&p, ws);
+
+  if (d->flags & HSV_FLAG_VALIDATE) {
+    if (hipMemsetAsync(p.err, 0, sizeof(int32_t), stream) != hipSuccess) return HSV_ERR_HIP;
+    if (launch_validate(p, stream) != hipSuccess) return HSV_ERR_HIP;
+    int32_t host_err = 0;
+    if (hipMemcpyAsync(&host_err, p.err, sizeof host_err, hipMemcpyDeviceToHost, stream) !=
+        hipSuccess)
+      return HSV_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return HSV_ERR_HIP;
+    if (host_err) return HSV_ERR_DEVICE_CHECK;
+  }
+  const uint32_t phase = d->flags & (HSV_FLAG_PHASE_PARTIALS | HSV_FLAG_PHASE_MERGE);
+  const bool run_partials = phase != HSV_FLAG_PHASE_MERGE;
+  const bool run_merge = phase != HSV_FLAG_PHASE_PARTIALS;
+  if (run_partials && p.n_parts > 0 && launch_attn_partials(p, stream) != hipSuccess)
+    return HSV_ERR_HIP;
+  if (run_merge && launch_merge_verify(p, stream) != hipSuccess) return HSV_ERR_HIP;
+  return HSV_OK;
+}
+
+}  // namespace
+
+AttnKernel choose_attn_kernel(const Plan &) { return AttnKernel::kValu; }
+
+hipError_t launch_attn_partials(const Plan &p, hipStream_t s) {
+  return launch_attn_partials_valu(p, s);
+}
+
+}  // namespace hsv
+
+using namespace hsv;
+
+extern "C" {
+
+hsv_status hsv_verify_workspace_bytes(const hsv_verify_desc *d, size_t *bytes) {
+  if (!d || !bytes) return HSV_ERR_NULL;
+  Plan p;
+  return make_plan(d, d->n_sel > 0, &p, bytes);
+}
+
+hsv_status hsv_verify_attn(const hsv_verify_desc *d, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *ctx_lens, const int32_t *parent,
+                           const uint64_t *anc_mask, void *o, float *lse, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return run_verify(d, false, q, k_cache, v_cache, ctx_lens, parent, anc_mask, nullptr, o, lse,
+                    workspace, workspace_bytes, stream);
+}
+
+hsv_status hsv_verify_attn_sparse(const hsv_verify_desc *d, const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *ctx_lens,
+                                  const int32_t *parent, const uint64_t *anc_mask,
+                                  const int32_t *kv_idx, void *o, float *lse, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return run_verify(d, true, q, k_cache, v_cache, ctx_lens, parent, anc_mask, kv_idx, o, lse,
+                    workspace, workspace_bytes, stream);
+}
+
+hsv_status hsv_tree_ancestor_mask(const int32_t *parent, uint64_t *anc_mask, int32_t batch,
+                                  int32_t n_draft, hipStream_t stream) {
+  if (!parent || !anc_mask) return HSV_ERR_NULL;
+  if (batch < 1 || n_draft < 1 || n_draft > 64) return HSV_ERR_SHAPE;
+  return launch_tree_mask(parent, anc_mask, batch, n_draft, stream) == hipSuccess ? HSV_OK
+                                                                                  : HSV_ERR_HIP;
+}
+
+hsv_status hsv_gather_kv(const void *k_cache, const void *v_cache, const int32_t *kv_idx,
+                         void *k_out, void *v_out, int32_t batch, int32_t n_kv_heads,
+                         int32_t kv_capacity, int32_t head_dim, int32_t n_sel, int32_t dtype,
+                         hipStream_t stream) {
+  if (!k_cache || !v_cache || !kv_idx || !k_out || !v_out) return HSV_ERR_NULL;
+  if (dtype != HSV_F32 && dtype != HSV_BF16) return HSV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return HSV_ERR_UNSUPPORTED;
+  if (batch < 1 || n_kv_heads < 1 || kv_capacity < 1 || n_sel < 1) return HSV_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * n_kv_heads > 65535) return HSV_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+       reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) % 16)
+    return HSV_ERR_SHAPE;
+  const int elem = dtype == HSV_F32 ? 4 : 2;
+  return launch_gather_kv(k_cache, v_cache, kv_idx, k_out, v_out, batch, n_kv_heads, kv_capacity,
+                          head_dim, n_sel, elem, stream) == hipSuccess
+             ? HSV_OK
+             : HSV_ERR_HIP;
+}
+
+hsv_status hsv_lse_merge(const float *o_parts, const float *lse_parts, int32_t n_parts,
+                         int64_t n_rows, int32_t head_dim, void *o, float *lse, int32_t out_dtype,
+                         hipStream_t stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return HSV_ERR_NULL;
+  if (n_parts < 1 || n_parts > 1024 || n_rows < 1) return HSV_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return HSV_ERR_UNSUPPORTED;
+  if (out_dtype != HSV_F32 && out_dtype != HSV_BF16) return HSV_ERR_UNSUPPORTED;
+  if (n_rows > (int64_t{1} << 40)) return HSV_ERR_SHAPE;
+  return launch_merge_rows(o_parts, lse_parts, n_parts, n_rows, head_dim, o, lse, out_dtype,
+                           stream) == hipSuccess
+             ? HSV_OK
+             : HSV_ERR_HIP;
+}
+
+const char *hsv_status_string(hsv_status s) {
+  switch (s) {
+    case HSV_OK: return "HSV_OK: success";
+    case HSV_ERR_NULL: return "HSV_ERR_NULL: a required pointer is NULL";
+    case HSV_ERR_SHAPE: return "HSV_ERR_SHAPE: sizes out of range or inconsistent";
+    case HSV_ERR_UNSUPPORTED: return "HSV_ERR_UNSUPPORTED: request not implemented by this build";
+    case HSV_ERR_WORKSPACE: return "HSV_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case HSV_ERR_DEVICE_CHECK: return "HSV_ERR_DEVICE_CHECK: device-side input check failed";
+    case HSV_ERR_HIP: return "HSV_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown hsv_status";
+}
+
+int32_t hsv_version(void) { return HSV_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Host-side launchers for the gfx950 kernels (one per kernel family).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace hsv {
+
+// Number of compute units the split heuristic plans for (MI355X: 8 XCDs x 32).
+constexpr int kPlanCUs = 256;
+
+// Which partial-attention kernel a plan runs.
+enum class AttnKernel { kValu, kMfma };
+
+AttnKernel choose_attn_kernel(const Plan &p);
+
+// Prefix splits and the tree part -> o_part / lse_part.
+hipError_t launch_attn_partials(const Plan &p, hipStream_t s);
+// Partials -> o [B, N, Hq, D], lse [B, N, Hq].
+hipError_t launch_merge_verify(const Plan &p, hipStream_t s);
+// Generic merge: o_parts [P, R, D], lse_parts [P, R] -> o [R, D], lse [R].
+hipError_t launch_merge_rows(const float *o_parts, const float *lse_parts, int n_parts,
+                             int64_t n_rows, int head_dim, void *o, float *lse, int out_dtype,
+                             hipStream_t s);
+hipError_t launch_tree_mask(const int32_t *parent, uint64_t *anc, int batch, int n_draft,
+                            hipStream_t s);
+hipError_t launch_gather_kv(const void *k, const void *v, const int32_t *idx, void *k_out,
+                            void *v_out, int batch, int hkv, int cap, int head_dim, int n_sel,
+                            int elem_bytes, hipStream_t s);
+// Device-side precondition check; ORs HSV-internal error bits into p.err.
+hipError_t launch_validate(const Plan &p, hipStream_t s);
+
+// Error bits written by the validation kernel.
+enum : int32_t {
+  kErrCtx = 1,     // ctx_lens[b] < 0, > max_ctx, or ctx + N > S_cap
+  kErrParent = 2,  // parent[b, i] outside [-1, i-1]
+  kErrIndex = 4,   // kv_idx not strictly increasing or outside [0, ctx_b)
+};
+
+}  // namespace hsv

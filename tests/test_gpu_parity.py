@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases compare every output element; the full-size workloads (in the
+launch configuration the benchmark times) compare sampled rows, which the
+oracle computes one by one.  Mask, index and gather handling must be
+bit-exact; O within 1e-2 max-abs and the LSE within 1e-3 relative.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from util import (assert_parity, cached_inputs, device_inputs, errors, log, run_hip, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hsv(gpu):
+    import long_context_tree_verify_amd as m
+    return m
+
+
+def _oracle_all(inp, **kw):
+    return oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                              kv_idx=inp.kv_idx, bf16=inp.is_bf16, **kw)
+
+
+# ----------------------------------------------------------------------------
+# a1: ancestor bitmask, bit-exact
+# ----------------------------------------------------------------------------
+
+def test_tree_mask_all_small_trees_bit_exact(hsv, gpu):
+    import itertools
+    import torch
+    for n in range(1, 7):
+        trees = np.array(list(itertools.product(*[range(-1, i) for i in range(n)])),
+                         dtype=np.int32)
+        ref = oracle.ancestor_mask(trees)
+        got = hsv.hsv_tree_ancestor_mask(torch.from_numpy(trees).to(gpu))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy().view(np.uint64), ref)
+    log(f"  all parent arrays with N <= 6 match")
+
+
+def test_tree_mask_large_trees_and_bad_parents(hsv, gpu):
+    import torch
+    rng = np.random.Generator(np.random.PCG64(77))
+    trees = [synth.random_tree_parents(rng, 64, max_depth=d, max_branch=64 if d <= 2 else 4)
+             for d in (1, 2, 6, 8, 64)]
+    trees += [synth.chain_parents(64), np.full(64, -1, np.int32),
+              synth.uniform_parents(rng, 64)]
+    trees = np.stack(trees).astype(np.int32)
+    got = hsv.hsv_tree_ancestor_mask(torch.from_numpy(trees).to(gpu)).cpu().numpy()
+    np.testing.assert_array_equal(got.view(np.uint64), oracle.ancestor_mask(trees))
+    bad = trees.copy()
+    bad[2, 10] = 10        # self-parent: invalid
+    got = hsv.hsv_tree_ancestor_mask(torch.from_numpy(bad).to(gpu)).cpu().numpy()
+    assert (got[2] == 0).all()
+    np.testing.assert_array_equal(got[[0, 1, 3]].view(np.uint64),
+                                  oracle.ancestor_mask(trees[[0, 1, 3]]))
+
+
+# ----------------------------------------------------------------------------
+# a2-a4: dense verification attention, small cases, every element
+# ----------------------------------------------------------------------------
+
+SMALL_CASES = [
+    ("tiny_tree", ()),                                                   # full size
+    ("tree32k", (("ctx", (3000, 3000)),)),                               # ragged tail
+    ("tree32k", (("ctx", (700, 700)), ("n_draft", 37), ("max_depth", 5))),
+    ("chain_b16", (("ctx", (500, 2100)), ("batch", 4))),
+    ("tree128k", (("ctx", (5000, 5000)),)),                              # x8 sinks
+    ("tree32k", (("ctx", (1000, 1000)), ("n_q_heads", 8), ("n_kv_heads", 8))),  # MHA, G=1
+    ("tree32k", (("ctx", (1500, 1500)), ("head_dim", 64), ("n_draft", 16))),
+    ("chain_b16", (("ctx", (0, 300)), ("batch", 6), ("n_draft", 1))),    # may hit c = 0
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL_CASES)
+def test_dense_parity_small(hsv, gpu, name, over):
+    inp = cached_inputs(name, over)
+    log(f"case {name} {dict(over)} ctx={inp.ctx_lens.tolist()[:6]}")
+    dev = device_inputs(inp, gpu)
+    o, lse = run_hip(hsv, inp, dev)
+    o_ref, l_ref = _oracle_all(inp)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, name)
+
+
+def test_tiny_fp32_is_tight(hsv, gpu):
+    inp = cached_inputs("tiny_tree")
+    dev = device_inputs(inp, gpu)
+    o, lse = run_hip(hsv, inp, dev)
+    o_ref, l_ref = _oracle_all(inp)
+    o_err, l_err = errors(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref)
+    assert o_err < 1e-5 and l_err < 1e-6
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 32, 0])
+def test_split_count_invariance(hsv, gpu, splits):
+    import torch
+    inp = cached_inputs("tree32k", (("ctx", (3000, 3000)),))
+    dev = device_inputs(inp, gpu)
+    o, lse = run_hip(hsv, inp, dev, num_splits=splits)
+    o1, l1 = run_hip(hsv, inp, dev, num_splits=1)
+    assert float((o - o1).abs().max()) <= 1e-5
+    assert float(((lse - l1).abs() / l1.abs().clamp(min=1)).max()) <= 1e-6
+    o_ref, l_ref = _oracle_all(inp)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"splits={splits}")
+    assert torch.isfinite(o).all()
+
+
+def test_deterministic_and_bf16_output_is_rne_of_fp32(hsv, gpu):
+    import torch
+    inp = cached_inputs("tree32k", (("ctx", (3000, 3000)),))
+    dev = device_inputs(inp, gpu)
+    o1, l1 = run_hip(hsv, inp, dev)
+    o2, l2 = run_hip(hsv, inp, dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ob, lb = run_hip(hsv, inp, dev, out_dtype=torch.bfloat16)
+    assert torch.equal(lb, l1)
+    rne = synth.f32_to_bf16_bits(o1.cpu().numpy())
+    np.testing.assert_array_equal(ob.cpu().view(torch.int16).numpy().view(np.uint16), rne)
+
+
+def test_parts_alone_match_oracle_parts(hsv, gpu):
+    inp = cached_inputs("tree32k", (("ctx", (3000, 3000)),))
+    dev = device_inputs(inp, gpu)
+    for flag, part in ((hsv.HSV_FLAG_NO_TREE, oracle.PART_PREFIX),
+                       (hsv.HSV_FLAG_NO_PREFIX, oracle.PART_TREE)):
+        o, lse = run_hip(hsv, inp, dev, flags=flag)
+        o_ref, l_ref = _oracle_all(inp, parts=part)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"flag={flag}")
+
+
+def test_ancestor_mask_input_and_general_masks(hsv, gpu):
+    import torch
+    inp = cached_inputs("tree32k", (("ctx", (3000, 3000)),))
+    dev = device_inputs(inp, gpu)
+    anc = oracle.ancestor_mask(inp.parent)
+    anc_dev = torch.from_numpy(anc.view(np.int64)).to(gpu)
+    o1, l1 = run_hip(hsv, inp, dev)
+    o2, l2 = run_hip(hsv, inp, dev, parent=None, anc=anc_dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # block-bidirectional masks (not a tree): 16-node blocks see each other
+    N = inp.wl.n_draft
+    blk = np.arange(N) // 16
+    anc2 = np.array([[sum(1 << j for j in range(N) if blk[j] == blk[i]) for i in range(N)]],
+                    dtype=np.uint64)
+    o3, l3 = run_hip(hsv, inp, dev, parent=None,
+                     anc=torch.from_numpy(anc2.view(np.int64)).to(gpu))
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, anc_mask=anc2,
+                                      bf16=True)
+    assert_parity(o3.cpu().numpy(), l3.cpu().numpy(), o_ref, l_ref, "block mask")
+
+
+# ----------------------------------------------------------------------------
+# a5: sparse verification attention and the gather
+# ----------------------------------------------------------------------------
+
+SPARSE_CASES = [
+    (("ctx", (8000, 8000)), ("batch", 2), ("n_sel", 1000), ("n_recent", 200)),
+    (("ctx", (3000, 3000)), ("batch", 3), ("n_sel", 77), ("n_recent", 10), ("n_draft", 5)),
+    (("ctx", (600, 600)), ("batch", 1), ("n_sel", 600), ("n_recent", 96)),   # all selected
+]
+
+
+@pytest.mark.parametrize("over", SPARSE_CASES)
+def test_sparse_parity_small_poisoned(hsv, gpu, over):
+    inp = cached_inputs("sparse64k", over, poison=True)
+    log(f"sparse case {dict(over)}")
+    dev = device_inputs(inp, gpu)
+    o, lse = run_hip(hsv, inp, dev)
+    o_ref, l_ref = _oracle_all(inp)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "sparse")
+
+
+def test_gather_kv_bit_exact(hsv, gpu):
+    import torch
+    inp = cached_inputs("sparse64k", SPARSE_CASES[0], poison=True)
+    dev = device_inputs(inp, gpu)
+    kg, vg = hsv.hsv_gather_kv(dev["k"], dev["v"], dev["kv_idx"])
+    torch.cuda.synchronize()
+    rk, rv = oracle.gather_kv(inp.k, inp.v, inp.kv_idx)
+    np.testing.assert_array_equal(kg.cpu().view(torch.int16).numpy().view(np.uint16), rk)
+    np.testing.assert_array_equal(vg.cpu().view(torch.int16).numpy().view(np.uint16), rv)
+
+
+# ----------------------------------------------------------------------------
+# a4 alone: the exported merge
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P,D", [(1, 64), (3, 128), (33, 128), (130, 64)])
+def test_lse_merge_matches_oracle(hsv, gpu, P, D):
+    import torch
+    rng = np.random.default_rng(P * 1000 + D)
+    R = 50
+    o_parts = rng.standard_normal((P, R, D)).astype(np.float32)
+    lse_parts = (rng.standard_normal((P, R)) * 3).astype(np.float32)
+    lse_parts[rng.random((P, R)) < 0.2] = -np.inf
+    lse_parts[:, 0] = -np.inf                     # an empty row
+    o_parts[np.isneginf(lse_parts)] = np.nan      # never read
+    o, lse = hsv.hsv_lse_merge(torch.from_numpy(o_parts).to(gpu),
+                               torch.from_numpy(lse_parts).to(gpu))
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    for r in range(R):
+        ro, rl = oracle.lse_merge(lse_parts[:, r].astype(np.float64),
+                                  np.nan_to_num(o_parts[:, r].astype(np.float64)))
+        if np.isneginf(rl):
+            assert np.isneginf(lse[r]) and (o[r] == 0).all()
+            continue
+        assert abs(lse[r] - rl) <= 1e-5 * max(1, abs(rl))
+        np.testing.assert_allclose(o[r], ro, rtol=0, atol=1e-5)
+
+
+# ----------------------------------------------------------------------------
+# validation flag (failure handling forced from the host; kernels exit normally)
+# ----------------------------------------------------------------------------
+
+def test_validate_flag(hsv, gpu):
+    import torch
+    inp = cached_inputs("chain_b16", (("ctx", (500, 2100)), ("batch", 4)))
+    dev = device_inputs(inp, gpu)
+    run_hip(hsv, inp, dev, flags=hsv.HSV_FLAG_VALIDATE)        # good data passes
+    bad_parent = dev["parent"].clone()
+    bad_parent[1, 3] = 5
+    with pytest.raises(hsv.HsvError) as e:
+        run_hip(hsv, inp, dev, parent=bad_parent, flags=hsv.HSV_FLAG_VALIDATE)
+    assert e.value.code == hsv.HSV_ERR_DEVICE_CHECK
+    sp = cached_inputs("sparse64k", SPARSE_CASES[1], poison=True)
+    sdev = device_inputs(sp, gpu)
+    run_hip(hsv, sp, sdev, flags=hsv.HSV_FLAG_VALIDATE)
+    bad_idx = sdev["kv_idx"].clone()
+    bad_idx[0, 0, 5] = bad_idx[0, 0, 4]                        # duplicate
+    sdev2 = dict(sdev, kv_idx=bad_idx)
+    with pytest.raises(hsv.HsvError) as e:
+        run_hip(hsv, sp, sdev2, flags=hsv.HSV_FLAG_VALIDATE)
+    assert e.value.code == hsv.HSV_ERR_DEVICE_CHECK
+    torch.cuda.synchronize()
