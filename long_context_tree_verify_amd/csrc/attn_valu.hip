@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void attn_partial_valu(Plan P) {
   // clamp the context so the draft block stays inside the cache, and drop
   // indices outside [0, c) (the validation flag reports both).
   const int c = min(max(P.ctx_lens[b], 0), P.cap - P.N);
-  const bool tree = part == P.tree_part;
+  const bool tree = part == P.tree_slot;
   int t_begin, t_end;
   uint64_t anc_i = 0;
   if (tree) {

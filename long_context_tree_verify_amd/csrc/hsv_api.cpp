@@ -14,8 +14,6 @@
 
 namespace hsv {
 
-hipError_t launch_attn_partials_valu(const Plan &p, hipStream_t s);
-
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -77,27 +75,52 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
 
   const bool with_prefix = !(d->flags & HSV_FLAG_NO_PREFIX);
   const bool with_tree = !(d->flags & HSV_FLAG_NO_TREE);
+
+  // Kernel variant: bf16 inputs run on the matrix cores, fp32 on the VALU.
+  int tile = kTile;
+  if (p->in_dtype == kBF16) {
+    p->kernel = p->R <= 32 ? kKernMfma32
+              : p->R <= 64 ? kKernMfma64
+              : p->R <= 128 ? kKernMfma128
+                            : kKernMfma256;
+    const MfmaShape sh = mfma_shape(p->kernel, p->D);
+    p->kgroups = sh.kgroups;
+    p->row_chunks = static_cast<int32_t>(ceil_div(p->R, sh.rows_per_wg));
+    tile = sh.tile_keys;
+  } else {
+    p->kernel = kKernValu;
+    p->kgroups = 1;
+    p->row_chunks = 1;
+  }
+
   const int64_t keys = sparse ? d->n_sel : d->max_ctx;
   if (with_prefix && keys > 0) {
-    int target;
+    int64_t target;
     if (d->num_splits > 0) {
       target = d->num_splits;
-    } else {
-      // Enough (b, kv head, split) work units to cover the GPU twice over,
-      // but no split shorter than four 64-key tiles.
+    } else if (p->kernel == kKernValu) {
       const int64_t units = static_cast<int64_t>(p->B) * p->Hkv;
-      const int64_t want = ceil_div(2 * kPlanCUs, units);
-      const int64_t by_len = ceil_div(keys, 4 * kTile);
-      target = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({want, by_len, kMaxSplits})));
+      target = std::min<int64_t>(ceil_div(2 * kPlanCUs, units), ceil_div(keys, 4 * tile));
+    } else {
+      // One workgroup per CU (each holds the CU's LDS); split the prefix so
+      // the (split, b, kv head, row chunk) workgroups cover the CUs, and
+      // split further while a split is longer than 64 tiles so that ragged
+      // contexts still balance.
+      const int64_t units = static_cast<int64_t>(p->B) * p->Hkv * p->row_chunks;
+      target = ceil_div(kPlanCUs, units);
+      while (ceil_div(keys, target * tile) > 64 && target * 2 <= kMaxSplits) target *= 2;
+      target = std::min<int64_t>(target, ceil_div(keys, tile));
     }
-    p->keys_per_split = static_cast<int32_t>(ceil_div(ceil_div(keys, target), kTile) * kTile);
-    p->n_splits = target;
+    target = std::max<int64_t>(1, std::min<int64_t>(target, kMaxSplits));
+    p->keys_per_split = static_cast<int32_t>(ceil_div(ceil_div(keys, target), tile) * tile);
+    p->n_splits = static_cast<int32_t>(target);
   } else {
     p->n_splits = 0;
-    p->keys_per_split = kTile;
+    p->keys_per_split = tile;
   }
-  p->tree_part = with_tree ? p->n_splits : -1;
-  p->n_parts = p->n_splits + (with_tree ? 1 : 0);
+  p->tree_slot = with_tree ? p->n_splits : -1;
+  p->n_slots = p->n_splits + (with_tree ? 1 : 0);
+  p->n_parts = p->n_slots * p->kgroups;
 
   const size_t rows = static_cast<size_t>(p->n_parts) * p->B * p->Hkv * p->R;
   size_t off = 0;
@@ -127,7 +150,7 @@ hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, cons
   size_t need = 0;
   hsv_status st = make_plan(d, sparse, &p, &need);
   if (st != HSV_OK) return st;
-  const bool with_tree = p.tree_part >= 0;
+  const bool with_tree = p.tree_slot >= 0;
   if (!q || !k || !v || !ctx_lens || !o || !lse) return HSV_ERR_NULL;
   if (sparse && !kv_idx) return HSV_ERR_NULL;
   if (with_tree && ((parent == nullptr) == (anc == nullptr))) return HSV_ERR_NULL;
@@ -169,10 +192,9 @@ hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, cons
 
 }  // namespace
 
-AttnKernel choose_attn_kernel(const Plan &) { return AttnKernel::kValu; }
-
 hipError_t launch_attn_partials(const Plan &p, hipStream_t s) {
-  return launch_attn_partials_valu(p, s);
+  return p.kernel == kKernValu ? launch_attn_partials_valu(p, s)
+                               : launch_attn_partials_mfma(p, s);
 }
 
 }  // namespace hsv

@@ -12,10 +12,16 @@ namespace hsv {
 // Number of compute units the split heuristic plans for (MI355X: 8 XCDs x 32).
 constexpr int kPlanCUs = 256;
 
-// Which partial-attention kernel a plan runs.
-enum class AttnKernel { kValu, kMfma };
+// Geometry of an MFMA partial-attention variant, for the planner.
+struct MfmaShape {
+  int kgroups;      // partial results per workgroup (waves along keys)
+  int tile_keys;    // keys per LDS tile; split lengths are multiples of it
+  int rows_per_wg;  // grouped query rows per workgroup
+};
+MfmaShape mfma_shape(int kernel, int head_dim);
 
-AttnKernel choose_attn_kernel(const Plan &p);
+hipError_t launch_attn_partials_valu(const Plan &p, hipStream_t s);
+hipError_t launch_attn_partials_mfma(const Plan &p, hipStream_t s);
 
 // Prefix splits and the tree part -> o_part / lse_part.
 hipError_t launch_attn_partials(const Plan &p, hipStream_t s);

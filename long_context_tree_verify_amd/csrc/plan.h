@@ -7,11 +7,21 @@ namespace hsv {
 
 enum : int { kF32 = 0, kBF16 = 1 };
 
+// Partial-attention kernel variants.
+enum : int {
+  kKernValu = 0,   // vector ALU, any dtype
+  kKernMfma32 = 1, // bf16 MFMA, <= 32 grouped rows, 4 key-waves
+  kKernMfma64 = 2, // bf16 MFMA, <= 64 grouped rows, 4 key-waves
+  kKernMfma128 = 3,// bf16 MFMA, <= 128 grouped rows, 2 row-waves x 2 key-waves
+  kKernMfma256 = 4 // bf16 MFMA, 256-row chunks, 4 row-waves
+};
+
 // One verify call, resolved on the host.  Grouped row r of KV head g is
 // (node i, query head g*G + hh) with r = i*G + hh; a KV head owns R = G*N
-// query rows.  Partial results are indexed by "part": parts [0, n_splits)
-// are contiguous key ranges of the prefix, part tree_part (if >= 0) is the
-// draft block under the tree mask.
+// query rows.  Keys are cut into "slots": slots [0, n_splits) are contiguous
+// ranges of the prefix (keys_per_split each), slot tree_slot (if >= 0) is the
+// draft block under the ancestor mask.  A workgroup of slot s writes
+// kgroups partial results, parts s*kgroups .. s*kgroups + kgroups-1.
 struct Plan {
   // inputs
   const void *q;
@@ -33,10 +43,14 @@ struct Plan {
   int32_t n_sel;            // > 0: sparse prefix
   int32_t max_ctx;
   int32_t in_dtype, out_dtype;
-  int32_t n_splits;         // prefix parts (0 when the prefix is left out)
-  int32_t keys_per_split;   // multiple of 64
-  int32_t tree_part;        // index of the tree part, or -1
-  int32_t n_parts;
+  int32_t kernel;           // kKern*
+  int32_t n_splits;         // prefix slots (0 when the prefix is left out)
+  int32_t keys_per_split;   // multiple of the kernel's key tile
+  int32_t tree_slot;        // slot index of the tree part, or -1
+  int32_t n_slots;          // n_splits + (tree_slot >= 0)
+  int32_t kgroups;          // partial results per slot workgroup
+  int32_t n_parts;          // n_slots * kgroups
+  int32_t row_chunks;       // workgroups per (slot, b, kv head) along rows
   float scale;              // score scale
   float scale_log2;         // scale * log2(e)
 };
