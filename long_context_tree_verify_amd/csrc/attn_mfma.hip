@@ -20,8 +20,7 @@
 // V is written to LDS transposed, with keys permuted (bits 2 and 3 of the key
 // index swapped inside each 16-key group) so that the eight keys a lane needs
 // for one P.V step are contiguous and come in as one 16-byte LDS read.
-// K rows and V^T rows are XOR-swizzled in 16-byte chunks against bank
-// conflicts.  Waves are arranged as RG row groups x KG key groups; each wave
+// K rows and V^T rows are padded by 16 bytes against bank conflicts.  Waves are arranged as RG row groups x KG key groups; each wave
 // writes its own partial (KG partials per slot), merged later with the rest.
 #include "common.hpp"
 #include "launch.h"
@@ -33,11 +32,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 
-template <int D_, int KG_, int QB_, int KBW_>
+template <int D_, int NW_, int KG_, int QB_, int KBW_>
 struct Cfg {
   static constexpr int D = D_;
+  static constexpr int NW = NW_;             // waves per workgroup
+  static constexpr int NT = NW_ * 64;        // threads per workgroup
   static constexpr int KG = KG_;             // waves along keys
-  static constexpr int RG = 4 / KG_;         // waves along rows
+  static constexpr int RG = NW_ / KG_;       // waves along rows
   static constexpr int QB = QB_;             // 32-query blocks per wave
   static constexpr int KBW = KBW_;           // 32-key blocks per wave per tile
   static constexpr int TK = 32 * KBW * KG;   // keys per tile
@@ -45,18 +46,25 @@ struct Cfg {
   static constexpr int CH = D / 8;           // 16-byte chunks per K/V row
   static constexpr int DK = D / 16;          // MFMA k-steps over the features
   static constexpr int DB = D / 32;          // 32-feature blocks of O
-  static constexpr int TILE_BYTES = TK * D * 2;          // K or V tile (bf16)
-  static constexpr int NKL = (TK * CH + 255) / 256;      // K loads per thread
-  static constexpr int NVG = (TK / 4 * CH + 255) / 256;  // 4-key V groups per thread
+  // LDS rows are padded by 16 bytes: 8 lanes reading the same 16-byte column
+  // of 8 consecutive rows then hit 8 different 4-bank groups, and every
+  // unrolled read is one base register plus an immediate offset.
+  static constexpr int KSTRIDE = D * 2 + 16;                // bytes per K row
+  static constexpr int VSTRIDE = TK * 2 + 16;               // bytes per V^T row
+  static constexpr int K_BYTES = TK * KSTRIDE;
+  static constexpr int V_BYTES = D * VSTRIDE;
+  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+  static constexpr int NKL = (TK * CH + NT - 1) / NT;       // K loads per thread
+  static constexpr int NVG = (TK / 4 * CH + NT - 1) / NT;   // 4-key V groups per thread
 };
+
+// Largest gap (log2 units) between a block maximum and the running softmax
+// reference before the reference moves: probabilities stay <= 2^8.
+constexpr float kSlack = 8.f;
 
 __device__ __forceinline__ int swap_bits23(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
-
-// XOR swizzle of a V^T row's 16-byte chunks: 8 consecutive feature rows read
-// the same logical chunk from 8 different banks.
-__device__ __forceinline__ int vt_swizzle(int d) { return (d ^ (d >> 3)) & 7; }
 
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);  // (b.lo << 16) | a.lo
@@ -71,46 +79,76 @@ struct Tile {
   uint4 v[C::NVG][4];
 };
 
-// Where key t of this slot lives in the cache, and whether it exists.
+// The keys of one slot: key t (t in [0, t_end)) is cache row idx[t] (sparse
+// prefix) or row off + t (dense prefix: off = 0; draft block: off = c).
 struct KeySource {
-  int mode;        // 0 dense prefix, 1 sparse prefix, 2 tree
-  int c;           // context length (clamped)
-  int t_end;       // keys [.., t_end) of this slot are valid
-  const int32_t *idx;
-  __device__ __forceinline__ int pos(int t, bool &valid) const {
-    valid = t < t_end;
-    if (!valid) return 0;
-    if (mode == 0) return t;
-    if (mode == 2) return c + t;
-    const int p = idx[t];
-    valid = p >= 0 && p < c;
-    return valid ? p : 0;
-  }
+  int off;
+  int t_end;
+  int c;                 // sparse rows must lie in [0, c)
+  const int32_t *idx;    // NULL unless a sparse prefix slot
 };
 
-template <class C>
+// Cache row of key t, or -1 when the key does not exist (past the slot's end
+// or an out-of-range index).  Never reads outside idx[0, t_end).
+template <bool SPARSE>
+__device__ __forceinline__ int key_row(const KeySource &src, int t) {
+  if (t >= src.t_end) return -1;
+  if (SPARSE && src.idx) {
+    const int p = src.idx[t];
+    return (p >= 0 && p < src.c) ? p : -1;
+  }
+  return src.off + t;
+}
+
+// Branch-free 16-byte load: invalid rows read row 0 of this (b, kv head) and
+// are replaced by zeros, so masked keys never carry NaN or stale data.
+__device__ __forceinline__ uint4 load_row_chunk(const uint4 *base, int row, int ch, int ch_per_row) {
+  const uint4 x = base[static_cast<int64_t>(row < 0 ? 0 : row) * ch_per_row + ch];
+  return row < 0 ? make_uint4(0, 0, 0, 0) : x;
+}
+
+template <class C, bool SPARSE>
 __device__ __forceinline__ void load_tile(Tile<C> &tl, const uint4 *kc, const uint4 *vc,
-                                          int64_t kv_row0, const KeySource &src, int t0,
-                                          int tid) {
+                                          const KeySource &src, int t0, int tid) {
+  if (!SPARSE && t0 + C::TK <= src.t_end) {
+    // a whole tile of contiguous rows: no per-key checks
+    const int row0 = src.off + t0;
+#pragma unroll
+    for (int i = 0; i < C::NKL; ++i) {
+      const int item = tid + C::NT * i;
+      if (C::TK * C::CH % C::NT != 0 && item >= C::TK * C::CH) break;
+      tl.k[i] = kc[static_cast<int64_t>(row0 + item / C::CH) * C::CH + item % C::CH];
+    }
+#pragma unroll
+    for (int i = 0; i < C::NVG; ++i) {
+      const int item = tid + C::NT * i;
+      const int grp = item % (C::TK / 4), ch = item / (C::TK / 4);
+      if (item < C::TK / 4 * C::CH) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          tl.v[i][r] = vc[static_cast<int64_t>(row0 + 4 * grp + r) * C::CH + ch];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::NKL; ++i) {
-    const int item = tid + 256 * i;
+    const int item = tid + C::NT * i;
     const int key = item / C::CH, ch = item % C::CH;
-    bool ok = item < C::TK * C::CH;
-    bool valid = false;
-    const int p = ok ? src.pos(t0 + key, valid) : 0;
-    tl.k[i] = valid ? kc[(kv_row0 + p) * C::CH + ch] : make_uint4(0, 0, 0, 0);
+    const int row = item < C::TK * C::CH ? key_row<SPARSE>(src, t0 + key) : -1;
+    tl.k[i] = load_row_chunk(kc, row, ch, C::CH);
   }
 #pragma unroll
   for (int i = 0; i < C::NVG; ++i) {
-    const int item = tid + 256 * i;
-    const int grp = item / C::CH, ch = item % C::CH;
+    const int item = tid + C::NT * i;
+    // groups vary fastest across lanes: the transposed 8-byte LDS writes of a
+    // wave then spread over a whole V^T row instead of one bank column
+    const int grp = item % (C::TK / 4), ch = item / (C::TK / 4);
     const bool ok = item < C::TK / 4 * C::CH;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      bool valid = false;
-      const int p = ok ? src.pos(t0 + 4 * grp + r, valid) : 0;
-      tl.v[i][r] = valid ? vc[(kv_row0 + p) * C::CH + ch] : make_uint4(0, 0, 0, 0);
+      const int row = ok ? key_row<SPARSE>(src, t0 + 4 * grp + r) : -1;
+      tl.v[i][r] = load_row_chunk(vc, row, ch, C::CH);
     }
   }
 }
@@ -119,16 +157,16 @@ template <class C>
 __device__ __forceinline__ void store_tile(const Tile<C> &tl, char *ks, char *vt, int tid) {
 #pragma unroll
   for (int i = 0; i < C::NKL; ++i) {
-    const int item = tid + 256 * i;
+    const int item = tid + C::NT * i;
     if (item >= C::TK * C::CH) break;
     const int key = item / C::CH, ch = item % C::CH;
-    *reinterpret_cast<uint4 *>(ks + key * C::CH * 16 + ((ch ^ (key & 7)) * 16)) = tl.k[i];
+    *reinterpret_cast<uint4 *>(ks + key * C::KSTRIDE + ch * 16) = tl.k[i];
   }
 #pragma unroll
   for (int i = 0; i < C::NVG; ++i) {
-    const int item = tid + 256 * i;
+    const int item = tid + C::NT * i;
     if (item >= C::TK / 4 * C::CH) break;
-    const int grp = item / C::CH, ch = item % C::CH;
+    const int grp = item % (C::TK / 4), ch = item / (C::TK / 4);
     const int p0 = swap_bits23(4 * grp);  // 4 consecutive positions p0..p0+3
     const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&tl.v[i][0]);
     const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&tl.v[i][1]);
@@ -146,15 +184,14 @@ __device__ __forceinline__ void store_tile(const Tile<C> &tl, char *ks, char *vt
         val.x = pack_lo(w0[w], w1[w]);
         val.y = pack_lo(w2[w], w3[w]);
       }
-      char *row = vt + d * (C::TK * 2);
-      *reinterpret_cast<uint2 *>(row + (((p0 >> 3) ^ vt_swizzle(d)) * 16) + (p0 & 7) * 2) = val;
+      *reinterpret_cast<uint2 *>(vt + d * C::VSTRIDE + p0 * 2) = val;
     }
   }
 }
 
-template <class C>
-__global__ __launch_bounds__(256, 1) void attn_partial_mfma(Plan P) {
-  __shared__ __attribute__((aligned(16))) char smem[2][2 * C::TILE_BYTES];
+template <class C, bool SPARSE>
+__global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
+  __shared__ __attribute__((aligned(16))) char smem[2][C::BUF_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -174,18 +211,19 @@ __global__ __launch_bounds__(256, 1) void attn_partial_mfma(Plan P) {
   const int c = min(max(P.ctx_lens[b], 0), P.cap - P.N);
   KeySource src;
   int t_begin;
+  src.c = c;
+  src.idx = nullptr;
   if (tree) {
-    src.mode = 2;
+    src.off = c;
     t_begin = 0;
     src.t_end = P.N;
   } else {
-    src.mode = P.n_sel > 0 ? 1 : 0;
-    const int lim = P.n_sel > 0 ? P.n_sel : c;
+    src.off = 0;
+    const int lim = SPARSE ? P.n_sel : c;
     t_begin = slot * P.keys_per_split;
     src.t_end = min(t_begin + P.keys_per_split, lim);
+    if (SPARSE) src.idx = P.kv_idx + static_cast<int64_t>(bg) * P.n_sel;
   }
-  src.c = c;
-  src.idx = P.n_sel > 0 ? P.kv_idx + static_cast<int64_t>(bg) * P.n_sel : nullptr;
   const int n_tiles = src.t_end > t_begin ? (src.t_end - t_begin + C::TK - 1) / C::TK : 0;
 
   // ---- this wave's query rows ----------------------------------------------
@@ -248,129 +286,127 @@ __global__ __launch_bounds__(256, 1) void attn_partial_mfma(Plan P) {
     l_run[qb] = 0.f;
   }
 
-  const uint4 *kc = static_cast<const uint4 *>(P.k);
-  const uint4 *vc = static_cast<const uint4 *>(P.v);
   const int64_t kv_row0 = static_cast<int64_t>(bg) * P.cap;
+  const uint4 *kc = static_cast<const uint4 *>(P.k) + kv_row0 * C::CH;
+  const uint4 *vc = static_cast<const uint4 *>(P.v) + kv_row0 * C::CH;
   const float cs = P.scale_log2;
   const int kbase = kg * 32 * C::KBW;
 
   Tile<C> tl;
-  load_tile<C>(tl, kc, vc, kv_row0, src, t_begin, tid);
-  store_tile<C>(tl, smem[0], smem[0] + C::TILE_BYTES, tid);
+  load_tile<C, SPARSE>(tl, kc, vc, src, t_begin, tid);
+  store_tile<C>(tl, smem[0], smem[0] + C::K_BYTES, tid);
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
     const int t0 = t_begin + j * C::TK;
     const bool more = j + 1 < n_tiles;
-    if (more) load_tile<C>(tl, kc, vc, kv_row0, src, t0 + C::TK, tid);
+    if (more) load_tile<C, SPARSE>(tl, kc, vc, src, t0 + C::TK, tid);
 
     const char *ks = smem[buf];
-    const char *vt = smem[buf] + C::TILE_BYTES;
+    const char *vt = smem[buf] + C::K_BYTES;
     const int nv = min(C::TK, src.t_end - t0);
 
-    // S^T = K . Q^T
-    floatx16 s[C::KBW][C::QB];
+    // One 32-key block at a time: S^T = K . Q^T, online softmax, O^T += V^T . P^T.
 #pragma unroll
-    for (int kb = 0; kb < C::KBW; ++kb)
+    for (int kb = 0; kb < C::KBW; ++kb) {
+      const int kb0 = kbase + 32 * kb;
+      floatx16 s[C::QB];
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) s[kb][qb] = floatx16{};
+      for (int qb = 0; qb < C::QB; ++qb) s[qb] = floatx16{};
+      {
+        const int key = kb0 + l32;
+        const char *krow = ks + key * C::KSTRIDE + hf * 16;
 #pragma unroll
-    for (int kstep = 0; kstep < C::DK; ++kstep) {
-      bf16x8 a[C::KBW];
+        for (int kstep = 0; kstep < C::DK; ++kstep) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + kstep * 32);
 #pragma unroll
-      for (int kb = 0; kb < C::KBW; ++kb) {
-        const int key = kbase + 32 * kb + l32;
-        const int chunk = 2 * kstep + hf;
-        a[kb] = *reinterpret_cast<const bf16x8 *>(ks + key * C::CH * 16 +
-                                                  ((chunk ^ (key & 7)) * 16));
+          for (int qb = 0; qb < C::QB; ++qb)
+            s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kstep], s[qb], 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int kb = 0; kb < C::KBW; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[qb][kstep], s[kb][qb],
-                                                               0, 0, 0);
-    }
 
-    // mask: keys past the slot's end, and the tree's non-ancestors
-    if (tree || nv < C::TK) {
+      // mask: keys past the slot's end, and the tree's non-ancestors.  The
+      // lane's 16 keys are kb0 + 4*hf + (8j + r); bit 8j + r of `keep` says
+      // whether that key is visible.
+      if (tree || kb0 + 32 > nv) {
+        const int room = nv - kb0 - 4 * hf;  // visible keys start at bit 0
+        uint32_t lim = room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
 #pragma unroll
-      for (int kb = 0; kb < C::KBW; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb)
+        for (int qb = 0; qb < C::QB; ++qb) {
+          uint32_t keep = lim;
+          if (tree) {
+            const int sh = kb0 + 4 * hf;
+            keep &= sh < 64 ? static_cast<uint32_t>(anc_q[qb] >> sh) : 0u;
+          }
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = kbase + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
-            bool ok = key < nv;
-            if (tree) ok = ok && ((anc_q[qb] >> (key & 63)) & 1u);
-            if (!ok) s[kb][qb][e] = kNegInf;
+            const int bit = 8 * (e >> 2) + (e & 3);
+            s[qb][e] = ((keep >> bit) & 1u) ? s[qb][e] : kNegInf;
           }
-    }
+        }
+      }
 
-    // online softmax (log2 domain), P^T packed to bf16 as the next B operand
-    bf16x8 pb[C::KBW][C::QB][2];
-    bool rescale = false;
-    float alpha[C::QB];
+      // Online softmax in the log2 domain.  The running reference m_run only
+      // moves when the block maximum exceeds it by more than kSlack (or on
+      // the first visible key), so O is rarely rescaled; any reference gives
+      // the same normalised result, and p <= 2^kSlack keeps fp32/bf16 safe.
+      // P^T is packed to bf16 as the next B operand.
+      bf16x8 pb[C::QB][2];
+      bool rescale = false;
+      float alpha[C::QB];
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      float mx = kNegInf;
+      for (int qb = 0; qb < C::QB; ++qb) {
+        float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < C::KBW; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[qb], mx * cs);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      alpha[qb] = fast_exp2(m_run[qb] - m_use);
-      rescale |= alpha[qb] != 1.f;
-      float sum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::KBW; ++kb) {
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * cs;
+        const bool move = mx > m_run[qb] + kSlack;
+        const float m_new = move ? mx : m_run[qb];
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        alpha[qb] = move ? fast_exp2(m_run[qb] - m_use) : 1.f;
+        // nothing to rescale before the first visible key: o_acc is still 0
+        rescale |= move && m_run[qb] != kNegInf;
+        float sum = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(fmaf(s[kb][qb][e], cs, -m_use));
-          s[kb][qb][e] = p;
+          const float p = fast_exp2(fmaf(s[qb][e], cs, -m_use));
+          s[qb][e] = p;
           sum += p;
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           floatx8 x;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = s[kb][qb][8 * half + e];
-          pb[kb][qb][half] = __builtin_convertvector(x, bf16x8);
+          for (int e = 0; e < 8; ++e) x[e] = s[qb][8 * half + e];
+          pb[qb][half] = __builtin_convertvector(x, bf16x8);
         }
+        l_run[qb] = l_run[qb] * alpha[qb] + sum;
+        m_run[qb] = m_new;
       }
-      l_run[qb] = l_run[qb] * alpha[qb] + sum;
-      m_run[qb] = m_new;
-    }
-    if (__any(rescale)) {
+      if (__builtin_expect(__any(rescale), 0)) {
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) o_acc[db][qb] *= alpha[qb];
-    }
+          for (int qb = 0; qb < C::QB; ++qb) o_acc[db][qb] *= alpha[qb];
+      }
 
-    // O^T += V^T . P^T
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const int d = 32 * db + l32;
-      const char *vrow = vt + d * (C::TK * 2);
-      const int sw = vt_swizzle(d);
-#pragma unroll
-      for (int kb = 0; kb < C::KBW; ++kb)
+      for (int db = 0; db < C::DB; ++db) {
+        const int d = 32 * db + l32;
+        const char *vrow = vt + d * C::VSTRIDE + hf * 16;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int pos = kbase + 32 * kb + 16 * half + 8 * hf;
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vrow + (((pos >> 3) ^ sw) * 16));
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vrow + (kb0 + 16 * half) * 2);
 #pragma unroll
           for (int qb = 0; qb < C::QB; ++qb)
-            o_acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][qb][half],
+            o_acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][half],
                                                                     o_acc[db][qb], 0, 0, 0);
         }
+      }
     }
 
-    if (more) store_tile<C>(tl, smem[buf ^ 1], smem[buf ^ 1] + C::TILE_BYTES, tid);
+    if (more) store_tile<C>(tl, smem[buf ^ 1], smem[buf ^ 1] + C::K_BYTES, tid);
     __syncthreads();
   }
 
@@ -402,18 +438,28 @@ __global__ __launch_bounds__(256, 1) void attn_partial_mfma(Plan P) {
 template <class C>
 hipError_t launch_cfg(const Plan &p, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(p.n_slots) * p.B * p.Hkv * p.row_chunks;
-  hipLaunchKernelGGL(attn_partial_mfma<C>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     p);
+  if (p.n_sel > 0)
+    hipLaunchKernelGGL((attn_partial_mfma<C, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(C::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_partial_mfma<C, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
+
+// Variants: <D, waves, key-waves, 32-query blocks per wave, 32-key blocks per wave>
+template <int D> using Cfg32 = Cfg<D, 4, 4, 1, 1>;   // <= 32 rows, 128-key tiles
+template <int D> using Cfg64 = Cfg<D, 8, 4, 1, 1>;   // <= 64 rows, 128-key tiles
+template <int D> using Cfg128 = Cfg<D, 8, 2, 1, 1>;  // <= 128 rows, 64-key tiles
+template <int D> using Cfg256 = Cfg<D, 8, 1, 1, 2>;  // 256-row chunks, 64-key tiles
 
 template <int D>
 hipError_t launch_d(const Plan &p, hipStream_t s) {
   switch (p.kernel) {
-    case kKernMfma32: return launch_cfg<Cfg<D, 4, 1, 1>>(p, s);
-    case kKernMfma64: return launch_cfg<Cfg<D, 4, 2, 1>>(p, s);
-    case kKernMfma128: return launch_cfg<Cfg<D, 2, 2, 1>>(p, s);
-    default: return launch_cfg<Cfg<D, 1, 2, 2>>(p, s);
+    case kKernMfma32: return launch_cfg<Cfg32<D>>(p, s);
+    case kKernMfma64: return launch_cfg<Cfg64<D>>(p, s);
+    case kKernMfma128: return launch_cfg<Cfg128<D>>(p, s);
+    default: return launch_cfg<Cfg256<D>>(p, s);
   }
 }
 
@@ -423,10 +469,10 @@ hipError_t launch_d(const Plan &p, hipStream_t s) {
 MfmaShape mfma_shape(int kernel, int head_dim) {
   (void)head_dim;
   switch (kernel) {
-    case kKernMfma32: return {4, 128, 32};
-    case kKernMfma64: return {4, 128, 64};
-    case kKernMfma128: return {2, 64, 128};
-    default: return {1, 64, 256};
+    case kKernMfma32: return {Cfg32<128>::KG, Cfg32<128>::TK, Cfg32<128>::ROWS};
+    case kKernMfma64: return {Cfg64<128>::KG, Cfg64<128>::TK, Cfg64<128>::ROWS};
+    case kKernMfma128: return {Cfg128<128>::KG, Cfg128<128>::TK, Cfg128<128>::ROWS};
+    default: return {Cfg256<128>::KG, Cfg256<128>::TK, Cfg256<128>::ROWS};
   }
 }
 
