@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libhsv.so")
 BUILD = os.path.join(ROOT, "_build", "hsv")
 ARCH = "gfx950"
 
-SOURCES = ["hsv_api.cpp", "attn_valu.hip", "attn_mfma.hip", "aux_kernels.hip"]
+SOURCES = ["hsv_api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_dma.hip", "aux_kernels.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

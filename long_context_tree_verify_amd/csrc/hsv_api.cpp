@@ -87,6 +87,12 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
     p->kgroups = sh.kgroups;
     p->row_chunks = static_cast<int32_t>(ceil_div(p->R, sh.rows_per_wg));
     tile = sh.tile_keys;
+    if (dma_supports(*p)) {
+      p->kernel = kKernDma256;
+      p->kgroups = 1;
+      p->row_chunks = static_cast<int32_t>(ceil_div(p->R, dma_rows_per_wg()));
+      tile = dma_tile_keys();
+    }
   } else {
     p->kernel = kKernValu;
     p->kgroups = 1;
@@ -193,8 +199,11 @@ hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, cons
 }  // namespace
 
 hipError_t launch_attn_partials(const Plan &p, hipStream_t s) {
-  return p.kernel == kKernValu ? launch_attn_partials_valu(p, s)
-                               : launch_attn_partials_mfma(p, s);
+  switch (p.kernel) {
+    case kKernValu: return launch_attn_partials_valu(p, s);
+    case kKernDma256: return launch_attn_partials_dma(p, s);
+    default: return launch_attn_partials_mfma(p, s);
+  }
 }
 
 }  // namespace hsv

@@ -22,6 +22,11 @@ MfmaShape mfma_shape(int kernel, int head_dim);
 
 hipError_t launch_attn_partials_valu(const Plan &p, hipStream_t s);
 hipError_t launch_attn_partials_mfma(const Plan &p, hipStream_t s);
+hipError_t launch_attn_partials_dma(const Plan &p, hipStream_t s);
+// The DMA-pipelined variant: dense bf16 prefix, head_dim 128, > 128 rows.
+bool dma_supports(const Plan &p);
+int dma_rows_per_wg();
+int dma_tile_keys();
 
 // Prefix splits and the tree part -> o_part / lse_part.
 hipError_t launch_attn_partials(const Plan &p, hipStream_t s);

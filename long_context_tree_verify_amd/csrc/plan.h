@@ -13,7 +13,8 @@ enum : int {
   kKernMfma32 = 1, // bf16 MFMA, <= 32 grouped rows, 4 key-waves
   kKernMfma64 = 2, // bf16 MFMA, <= 64 grouped rows, 4 key-waves
   kKernMfma128 = 3,// bf16 MFMA, <= 128 grouped rows, 2 row-waves x 2 key-waves
-  kKernMfma256 = 4 // bf16 MFMA, 256-row chunks, 4 row-waves
+  kKernMfma256 = 4,// bf16 MFMA, 256-row chunks, register-staged tiles
+  kKernDma256 = 5  // bf16 MFMA, 256-row chunks, HBM->LDS DMA pipeline (dense, D=128)
 };
 
 // One verify call, resolved on the host.  Grouped row r of KV head g is
