@@ -57,6 +57,12 @@ constexpr int kStages = 4;
 constexpr int kBlocks = kTileBytes / 1024;     // 1 KB DMA blocks per K (or V) tile
 constexpr int kBlocksPerWave = kBlocks / kNW;  // per wave, for K and again for V
 constexpr int kDmaPerTile = 2 * kBlocksPerWave;  // DMA instructions per thread per tile
+// Epilogue staging: every wave's 32 x 128 fp32 partial, rows padded by 16 B.
+constexpr int kEpiRowStride = kD * 4 + 16;
+constexpr int kSmemBytes = kStages * kStageBytes > kNW * 32 * kEpiRowStride
+                               ? kStages * kStageBytes
+                               : kNW * 32 * kEpiRowStride;
+
 // Largest per-lane sum of 16 probabilities the fast softmax path accepts
 // (each probability then stays <= 2^16, far from fp32/bf16 overflow).
 constexpr float kSumLimit = 65536.f;
@@ -107,7 +113,7 @@ __device__ __forceinline__ void wait_tile_and_sync(bool next_in_flight) {
 }
 
 __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   static_assert(kStages == 4, "tile j+2 is fetched while tiles j-1, j, j+1 stay resident");
 
   const int tid = threadIdx.x;
@@ -347,22 +353,36 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   }
 
   // ---- epilogue --------------------------------------------------------------
+  // Normalise, then write the wave's 32 x 128 partial through LDS so that the
+  // global stores are whole 512-byte rows (lane l holds a query column; rows
+  // are padded by 16 bytes so the column-wise LDS writes spread over banks).
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (r < P.R) {
-    float *dst = P.o_part + prow * kD;
+  if (hf == 0 && r < P.R)
+    P.lse_part[prow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+  constexpr int kRowStride = kEpiRowStride;
+  __syncthreads();  // every wave is done with the K/V stages
+  char *ep = smem + wave * 32 * kRowStride;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float4 v4;
-        v4.x = o_acc[db][4 * jj + 0] * inv;
-        v4.y = o_acc[db][4 * jj + 1] * inv;
-        v4.z = o_acc[db][4 * jj + 2] * inv;
-        v4.w = o_acc[db][4 * jj + 3] * inv;
-        *reinterpret_cast<float4 *>(dst + 32 * db + 8 * jj + 4 * hf) = v4;
-      }
-    if (hf == 0) P.lse_part[prow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    for (int jj = 0; jj < 4; ++jj) {
+      float4 v4;
+      v4.x = o_acc[db][4 * jj + 0] * inv;
+      v4.y = o_acc[db][4 * jj + 1] * inv;
+      v4.z = o_acc[db][4 * jj + 2] * inv;
+      v4.w = o_acc[db][4 * jj + 3] * inv;
+      *reinterpret_cast<float4 *>(ep + l32 * kRowStride + (32 * db + 8 * jj + 4 * hf) * 4) = v4;
+    }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  float *dst0 = P.o_part + (prow - l32) * kD;  // row row_base of this wave
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = 2 * it + (lane >> 5);  // two rows per instruction
+    const float4 v4 = *reinterpret_cast<const float4 *>(ep + row * kRowStride + (lane & 31) * 16);
+    if (row_base + row < P.R)
+      *reinterpret_cast<float4 *>(dst0 + row * kD + (lane & 31) * 4) = v4;
   }
 }
 

@@ -22,18 +22,23 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t *parent, ui
 
 // --------------------------------------------------------------------------
 // Log-sum-exp merge (LongSpec section 2.C: exact combination of the parts).
-// One wave per output row; lane <-> feature.  Weights exp(lse_p - lse) are
-// computed once per part (lane <-> part) and broadcast with v_readlane.
-// Parts whose lse is -inf are skipped without reading their o.
+// One wave per output row; lane l owns features 2l, 2l+1 (D = 128) or l
+// (D = 64).  Lane p reads part p's LSE, the wave reduces them to
+// lse = m + log sum exp(lse_p - m), and the per-part weights exp(lse_p - lse)
+// are broadcast with v_readlane while eight parts' rows are in flight.
+// Parts with lse = -inf get weight 0 and their (possibly never written) o
+// rows are discarded by a select, so they cannot inject NaN.
 // --------------------------------------------------------------------------
+constexpr int kMergeRowsPerBlock = 4;  // 256 threads, one wave per row
+
 template <int D>
 __device__ __forceinline__ void merge_row(const float *o_parts, const float *lse_parts,
                                           int n_parts, int64_t part_stride_rows, int64_t row,
-                                          float (&acc)[D / kWave], float *lse_out, int lane) {
-  constexpr int DL = D / kWave;
+                                          int lane, float (&acc)[D / 64], float *lse_out) {
+  constexpr int DL = D / 64;
+  const float *lp = lse_parts + row;
   float m = kNegInf;
-  for (int p = lane; p < n_parts; p += kWave)
-    m = fmaxf(m, lse_parts[p * part_stride_rows + row]);
+  for (int p = lane; p < n_parts; p += kWave) m = fmaxf(m, lp[p * part_stride_rows]);
   m = wave_max(m);
 #pragma unroll
   for (int j = 0; j < DL; ++j) acc[j] = 0.f;
@@ -42,23 +47,33 @@ __device__ __forceinline__ void merge_row(const float *o_parts, const float *lse
     return;
   }
   float sum = 0.f;
-  for (int p = lane; p < n_parts; p += kWave) {
-    const float lp = lse_parts[p * part_stride_rows + row];
-    sum += fast_exp2((lp - m) * kLog2e);  // exp2(-inf) = 0 for empty parts
-  }
+  for (int p = lane; p < n_parts; p += kWave)
+    sum += fast_exp2((lp[p * part_stride_rows] - m) * kLog2e);
   sum = wave_sum(sum);
   const float lse = m + fast_log2(sum) * kLn2;
+  const float *op = o_parts + row * D + lane * DL;
+  const int64_t ostride = part_stride_rows * D;
+  constexpr int kBatch = 8;
   for (int p0 = 0; p0 < n_parts; p0 += kWave) {
     const int p = p0 + lane;
-    const float lp = p < n_parts ? lse_parts[p * part_stride_rows + row] : kNegInf;
-    const float w = fast_exp2((lp - lse) * kLog2e);
+    const float w_lane = p < n_parts ? fast_exp2((lp[p * part_stride_rows] - lse) * kLog2e) : 0.f;
     const int n_here = min(kWave, n_parts - p0);
-    for (int jj = 0; jj < n_here; ++jj) {
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), jj));
-      if (wj == 0.f) continue;
-      const float *src = o_parts + ((p0 + jj) * part_stride_rows + row) * D;
+    for (int u0 = 0; u0 < n_here; u0 += kBatch) {
+      float w[kBatch];
+      float v[kBatch][DL];
 #pragma unroll
-      for (int j = 0; j < DL; ++j) acc[j] = fmaf(wj, src[lane + j * kWave], acc[j]);
+      for (int u = 0; u < kBatch; ++u) {
+        const int q = min(p0 + u0 + u, n_parts - 1);  // stays in bounds
+        w[u] = u0 + u < n_here
+                   ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), u0 + u))
+                   : 0.f;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) v[u][j] = op[q * ostride + j];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int j = 0; j < DL; ++j) acc[j] = fmaf(w[u], w[u] != 0.f ? v[u][j] : 0.f, acc[j]);
     }
   }
   *lse_out = lse;
@@ -66,23 +81,23 @@ __device__ __forceinline__ void merge_row(const float *o_parts, const float *lse
 
 template <int D>
 __device__ __forceinline__ void store_row(void *o, int out_dtype, int64_t base,
-                                          const float (&acc)[D / kWave], int lane) {
-  constexpr int DL = D / kWave;
+                                          const float (&acc)[D / 64], int lane) {
+  constexpr int DL = D / 64;
   if (out_dtype == kF32) {
-    float *dst = static_cast<float *>(o) + base;
+    float *dst = static_cast<float *>(o) + base + lane * DL;
 #pragma unroll
-    for (int j = 0; j < DL; ++j) dst[lane + j * kWave] = acc[j];
+    for (int j = 0; j < DL; ++j) dst[j] = acc[j];
   } else {
-    uint16_t *dst = static_cast<uint16_t *>(o) + base;
+    uint16_t *dst = static_cast<uint16_t *>(o) + base + lane * DL;
 #pragma unroll
-    for (int j = 0; j < DL; ++j) dst[lane + j * kWave] = f32_to_bf16_rne(acc[j]);
+    for (int j = 0; j < DL; ++j) dst[j] = f32_to_bf16_rne(acc[j]);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void merge_verify_kernel(Plan P) {
   const int lane = threadIdx.x % kWave;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + threadIdx.x / kWave;
   const int64_t total = static_cast<int64_t>(P.B) * P.N * P.Hq;
   if (row >= total) return;
   const int h = static_cast<int>(row % P.Hq);
@@ -92,9 +107,9 @@ __global__ __launch_bounds__(256) void merge_verify_kernel(Plan P) {
   const int r = i * P.G + (h % P.G);
   const int64_t prow = (static_cast<int64_t>(b) * P.Hkv + g) * P.R + r;
   const int64_t stride = static_cast<int64_t>(P.B) * P.Hkv * P.R;
-  float acc[D / kWave];
+  float acc[D / 64];
   float lse;
-  merge_row<D>(P.o_part, P.lse_part, P.n_parts, stride, prow, acc, &lse, lane);
+  merge_row<D>(P.o_part, P.lse_part, P.n_parts, stride, prow, lane, acc, &lse);
   store_row<D>(P.o, P.out_dtype, row * D, acc, lane);
   if (lane == 0) P.lse[row] = lse;
 }
@@ -105,11 +120,11 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float *o_parts,
                                                          int64_t n_rows, void *o, float *lse,
                                                          int out_dtype) {
   const int lane = threadIdx.x % kWave;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + threadIdx.x / kWave;
   if (row >= n_rows) return;
-  float acc[D / kWave];
+  float acc[D / 64];
   float l;
-  merge_row<D>(o_parts, lse_parts, n_parts, n_rows, row, acc, &l, lane);
+  merge_row<D>(o_parts, lse_parts, n_parts, n_rows, row, lane, acc, &l);
   store_row<D>(o, out_dtype, row * D, acc, lane);
   if (lane == 0) lse[row] = l;
 }
@@ -177,7 +192,7 @@ hipError_t launch_tree_mask(const int32_t *parent, uint64_t *anc, int batch, int
 
 hipError_t launch_merge_verify(const Plan &p, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(p.B) * p.N * p.Hq;
-  dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  dim3 grid(static_cast<unsigned>((rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock));
   if (p.D == 64)
     hipLaunchKernelGGL(merge_verify_kernel<64>, grid, dim3(256), 0, s, p);
   else
@@ -188,7 +203,7 @@ hipError_t launch_merge_verify(const Plan &p, hipStream_t s) {
 hipError_t launch_merge_rows(const float *o_parts, const float *lse_parts, int n_parts,
                              int64_t n_rows, int head_dim, void *o, float *lse, int out_dtype,
                              hipStream_t s) {
-  dim3 grid(static_cast<unsigned>((n_rows + 3) / 4));
+  dim3 grid(static_cast<unsigned>((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock));
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_rows_kernel<64>, grid, dim3(256), 0, s, o_parts, lse_parts,
                        n_parts, n_rows, o, lse, out_dtype);
