@@ -6,9 +6,9 @@
 // domain); what differs is how K and V reach the matrix cores:
 //
 //  * global_load_lds_dwordx4 moves each 16-byte chunk straight into LDS (no
-//    staging registers), so a workgroup keeps two tiles of 64 keys in
+//    staging registers), so a workgroup keeps kAhead tiles of 64 keys in
 //    flight while it computes on another -- the memory-level parallelism the
-//    HBM stream needs (prefetch distance two; see the main loop for why).
+//    HBM stream needs.
 //  * Each DMA instruction fills 1 KB: 16 keys x 4 consecutive 16-byte chunks.
 //    A tile is 16 such blocks for K and 16 for V, block b = (key/16)*4 +
 //    chunk/4.  Inside a K block the order is (chunk%4)*256 + (key%16)*16, so
@@ -16,6 +16,9 @@
 //    inside a V block it is (key%16)*64 + (chunk%4)*16, so each half-wave of
 //    a transpose read covers 256 contiguous bytes.  Every LDS read below is
 //    one lane base register plus an immediate.
+//  * The DMA addresses are a scalar base (the tile's first cache row) plus a
+//    per-lane 32-bit byte offset that is the same for every full tile, so
+//    issuing a tile costs no vector address arithmetic.
 //  * V stays row-major in LDS; the V^T operand of P.V comes from
 //    ds_read_b64_tr_b16, which hands each lane of a 16-lane group one b16
 //    element from each of four other lanes' 8-byte rows: lane s of a group
@@ -29,6 +32,8 @@
 //    consumed before the first DMA is issued, so the compiler's own vmcnt
 //    waits never cover an unknown DMA count.  M0 (the LDS base of the DMA) is
 //    set inside the same asm statement; the kernel uses M0 for nothing else.
+//  * The V^T operands of a key block are read before its softmax, so their
+//    LDS latency overlaps the exponentials.
 //
 // Rows of keys outside the slot are fetched from the slot's last valid row
 // (so every address is inside the cache and every staged value is a real,
@@ -45,15 +50,18 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 constexpr int kNW = 8;              // waves: 8 x 32 query rows
 constexpr int kNT = kNW * 64;
 constexpr int kTK = 64;             // keys per tile
 constexpr int kD = 128;
-constexpr int kCH = kD / 8;         // 16-byte chunks per row
-constexpr int kTileBytes = kTK * kD * 2;       // 16 KB (K or V)
+constexpr int kRowBytes = kD * 2;   // one bf16 cache row
+constexpr int kTileBytes = kTK * kRowBytes;    // 16 KB (K or V)
 constexpr int kStageBytes = 2 * kTileBytes;    // K then V
 constexpr int kStages = 4;
+constexpr int kAhead = 2;           // tiles in flight beyond the one computed on
+static_assert(kAhead + 1 <= kStages, "the stage refilled was read one iteration earlier");
 constexpr int kBlocks = kTileBytes / 1024;     // 1 KB DMA blocks per K (or V) tile
 constexpr int kBlocksPerWave = kBlocks / kNW;  // per wave, for K and again for V
 constexpr int kDmaPerTile = 2 * kBlocksPerWave;  // DMA instructions per thread per tile
@@ -67,46 +75,34 @@ constexpr int kSmemBytes = kStages * kStageBytes > kNW * 32 * kEpiRowStride
 // (each probability then stays <= 2^16, far from fp32/bf16 overflow).
 constexpr float kSumLimit = 65536.f;
 
-// 16 bytes per lane from global memory straight into LDS at `lds` + 16*lane
-// (the LDS base is wave-uniform and goes through M0).
-__device__ __forceinline__ void dma16(const void *gptr, lds_char *lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
+// (lds_base is wave-uniform and goes through M0).  Address = sbase + voff.
+// (M0 is clobbered on purpose: nothing else in these kernels uses it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char *sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(gptr), "s"(base)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
       : "memory", "m0");
 }
-
-// This thread's DMA of one tile: kBlocksPerWave K blocks and as many V blocks.
-__device__ __forceinline__ void issue_tile(const uint4 *kc, const uint4 *vc, int row_first,
-                                           int row_last, int lane, int wave, lds_char *stage) {
-#pragma unroll
-  for (int bw = 0; bw < kBlocksPerWave; ++bw) {
-    const int blk = wave * kBlocksPerWave + bw;
-    // K block: (chunk%4)*256 + (key%16)*16 -- lane i: key i%16, chunk i/16
-    const int kkey = (blk >> 2) * 16 + (lane & 15);
-    const int kchunk = (blk & 3) * 4 + (lane >> 4);
-    const int krow = min(row_first + kkey, row_last);
-    dma16(kc + static_cast<int64_t>(krow) * kCH + kchunk, stage + blk * 1024);
-    // V block: (key%16)*64 + (chunk%4)*16 -- lane i: key i/4, chunk i%4
-    const int vkey = (blk >> 2) * 16 + (lane >> 2);
-    const int vchunk = (blk & 3) * 4 + (lane & 3);
-    const int vrow = min(row_first + vkey, row_last);
-    dma16(vc + static_cast<int64_t>(vrow) * kCH + vchunk, stage + kTileBytes + blk * 1024);
-  }
-}
+#pragma clang diagnostic pop
 
 // Wait until this thread's DMA of the current tile is done (the next tile's
 // may still be in flight), then meet the other waves: their DMA of the
 // current tile is then in LDS too, and they are done reading the stage the
 // next DMA will overwrite.
-__device__ __forceinline__ void wait_tile_and_sync(bool next_in_flight) {
-  static_assert(kDmaPerTile == 4, "the immediate below assumes 4 DMA ops per tile");
-  if (next_in_flight)
+// `later` = tiles issued after the current one (0 .. kAhead - 1 outstanding
+// beyond it).
+__device__ __forceinline__ void wait_tile_and_sync(int later) {
+  static_assert(kDmaPerTile == 4, "the immediates below assume 4 DMA ops per tile");
+  static_assert(kAhead <= 3, "immediates below");
+  if (later >= 2)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if (later == 1)
     asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -114,10 +110,10 @@ __device__ __forceinline__ void wait_tile_and_sync(bool next_in_flight) {
 
 __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  static_assert(kStages == 4, "tile j+2 is fetched while tiles j-1, j, j+1 stay resident");
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
   const int l32 = lane & 31, hf = lane >> 5;
 
   int bid = blockIdx.x;
@@ -127,22 +123,20 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   const int bg = bid % BH;
   const int slot = bid / BH;
   const int b = bg / P.Hkv, g = bg % P.Hkv;
-  const bool tree = slot == P.tree_slot;
 
-  // ---- key range of this slot: cache rows [row_lo + t] for t in [t_begin, t_end)
+  // ---- key range of this slot: cache rows [t_begin, t_end) -----------------
+  // The prefix rows [0, c) and the draft rows [c, c + N) form one range
+  // [lo, hi); rows at or past c are visible to a query only through its
+  // ancestor bits.
   const int c = min(max(P.ctx_lens[b], 0), P.cap - P.N);
-  int t_begin, t_end, row_off;
-  if (tree) {
-    t_begin = 0;
-    t_end = P.N;
-    row_off = c;
-  } else {
-    t_begin = slot * P.keys_per_split;
-    t_end = min(t_begin + P.keys_per_split, c);
-    row_off = 0;
-  }
+  const int lo = P.has_prefix ? 0 : c;
+  const int hi = P.has_tree ? c + P.N : c;
+  const int t_begin = lo + slot * P.keys_per_split;
+  const int t_end = min(t_begin + P.keys_per_split, hi);
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTK - 1) / kTK : 0;
-  const int row_last = row_off + t_end - 1;  // last valid row: clamp target
+  const int row_last = t_end - 1;      // last valid row: clamp target
+  const bool tree = t_end > c;         // the range reaches the draft rows
+  const int mask_from = min(c, t_end); // blocks reaching past this row are masked
 
   const int row_base = rc * (kNW * 32) + wave * 32;
   const int r = row_base + l32;
@@ -154,11 +148,56 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     return;
   }
 
+  // byte bases of this (batch, kv head)'s cache rows
   const int64_t kv_row0 = static_cast<int64_t>(bg) * P.cap;
-  const uint4 *kc = static_cast<const uint4 *>(P.k) + kv_row0 * kCH;
-  const uint4 *vc = static_cast<const uint4 *>(P.v) + kv_row0 * kCH;
+  const char *kbytes = static_cast<const char *>(P.k) + kv_row0 * kRowBytes;
+  const char *vbytes = static_cast<const char *>(P.v) + kv_row0 * kRowBytes;
   // C-style cast: the generic -> LDS address-space conversion
   lds_char *const lds = (lds_char *)(smem);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+
+  // ---- DMA lane offsets ------------------------------------------------------
+  // K block blk: lane i carries key (blk/4)*16 + i%16, chunk (blk%4)*4 + i/16;
+  // V block blk: key (blk/4)*16 + i/4, chunk (blk%4)*4 + i%4.
+  int krel[kBlocksPerWave], vrel[kBlocksPerWave];
+  uint32_t kch[kBlocksPerWave], vch[kBlocksPerWave];
+#pragma unroll
+  for (int bw = 0; bw < kBlocksPerWave; ++bw) {
+    const int blk = wave * kBlocksPerWave + bw;
+    krel[bw] = (blk >> 2) * 16 + (lane & 15);
+    kch[bw] = ((blk & 3) * 4 + (lane >> 4)) * 16;
+    vrel[bw] = (blk >> 2) * 16 + (lane >> 2);
+    vch[bw] = ((blk & 3) * 4 + (lane & 3)) * 16;
+  }
+  // This thread's DMA of tile j into stage j % kStages.
+  auto issue_tile = [&](const int j) {
+    const int row_first = t_begin + j * kTK;
+    const int lim = row_last - row_first;  // last valid key of the tile
+    const char *kt = kbytes + static_cast<int64_t>(row_first) * kRowBytes;
+    const char *vt = vbytes + static_cast<int64_t>(row_first) * kRowBytes;
+    const uint32_t st = lds0 + (j % kStages) * kStageBytes;
+    if (lim >= kTK - 1) {
+#pragma unroll
+      for (int bw = 0; bw < kBlocksPerWave; ++bw) {
+        const uint32_t blk_off = (wave * kBlocksPerWave + bw) * 1024;
+        dma16(kt, krel[bw] * kRowBytes + kch[bw], st + blk_off);
+        dma16(vt, vrel[bw] * kRowBytes + vch[bw], st + kTileBytes + blk_off);
+      }
+    } else {
+#pragma unroll
+      for (int bw = 0; bw < kBlocksPerWave; ++bw) {
+        const uint32_t blk_off = (wave * kBlocksPerWave + bw) * 1024;
+        dma16(kt, min(krel[bw], lim) * kRowBytes + kch[bw], st + blk_off);
+        dma16(vt, min(vrel[bw], lim) * kRowBytes + vch[bw], st + kTileBytes + blk_off);
+      }
+    }
+  };
+
+  // prologue: tiles 0 .. kAhead-1 in flight, issued before the query loads so
+  // the two latencies overlap
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    if (j < n_tiles) issue_tile(j);
 
   // ---- this lane's query (B operand of S^T = K.Q^T), tree mask word --------
   const uint4 *qv = static_cast<const uint4 *>(P.q);
@@ -171,7 +210,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     const int64_t qrow = (static_cast<int64_t>(b) * P.N + i) * P.Hq + h;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint4 u = ok ? qv[qrow * kCH + 2 * ks + hf] : make_uint4(0, 0, 0, 0);
+      const uint4 u = ok ? qv[qrow * (kD / 8) + 2 * ks + hf] : make_uint4(0, 0, 0, 0);
       qf[ks] = __builtin_bit_cast(bf16x8, u);
     }
     if (tree) {
@@ -186,15 +225,11 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     }
   }
 
-  // Consume the query (and tree) loads now: the compiler's wait for them then
-  // happens before the first DMA is in flight.
+  // Consume the query (and tree) loads now.  The compiler does not count the
+  // DMA, so its wait here is vmcnt(0): the prologue tiles have landed too.
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
   asm volatile("" ::"v"(anc_q));
-
-  // prologue: tiles 0 and 1 in flight (prefetch distance two)
-  issue_tile(kc, vc, row_off + t_begin, row_last, lane, wave, lds);
-  if (n_tiles > 1) issue_tile(kc, vc, row_off + t_begin + kTK, row_last, lane, wave, lds + kStageBytes);
 
   // lane bases of the LDS reads (byte offsets inside a stage)
   const int k_base = (l32 >> 4) * 4096 + hf * 256 + (l32 & 15) * 16;
@@ -208,35 +243,67 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   float m_run = kNegInf, l_run = 0.f;
   const float cs = P.scale_log2;
 
-  // S^T = K . Q^T for the two 32-key blocks of the tile in stage `st`; all K
-  // operands are read first so the LDS latency overlaps the matrix work.
+  // S^T = K . Q^T for the two 32-key blocks of the tile in stage `st`.
   auto qk = [&](lds_char *const st, floatx16 (&sv)[2]) {
-    bf16x8 ka[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        ka[kb][ks] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
-            st + k_base + kb * 8192 + (ks >> 1) * 1024 + (ks & 1) * 512);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 ka[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        ka[ks] = *(const lds_bf16x8 *)(st + k_base + kb * 8192 + (ks >> 1) * 1024 + (ks & 1) * 512);
       sv[kb] = floatx16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qf[ks], sv[kb], 0, 0, 0);
+        sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sv[kb], 0, 0, 0);
     }
   };
 
-  // Mask and softmax of one 32-key block (keys kb0 .. kb0+31 of a tile with
-  // nv valid keys); returns the block's P^T as two bf16 B operands.
-  auto softmax = [&](floatx16 &sv, const int kb0, const int nv, bf16x8 (&pb)[2]) {
-    if (tree || kb0 + 32 > nv) {
-      const int room = nv - kb0 - 4 * hf;
-      uint32_t keep = room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
-      if (tree) {
-        const int sh = kb0 + 4 * hf;
-        keep &= sh < 64 ? static_cast<uint32_t>(anc_q >> sh) : 0u;
+  // V^T operands of key block kb (two transpose reads per operand).
+  auto read_v = [&](lds_char *const st, const int kb, bf16x8 (&va)[4][2]) {
+    bf16x4 t[4][2][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        lds_char *vp = st + v_base + (kb * 2 + half) * 4096 + db * 1024;
+        t[db][half][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp));
+        t[db][half][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp + 512));
       }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        va[db][half] = __builtin_shufflevector(t[db][half][0], t[db][half][1], 0, 1, 2, 3, 4, 5,
+                                               6, 7);
+  };
+
+  auto to_bf16 = [&](const float (&p)[16], bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      floatx8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = p[8 * half + e];
+      pb[half] = __builtin_convertvector(x, bf16x8);
+    }
+  };
+
+  // Mask and softmax of one 32-key block (cache rows t0 .. t0+31); returns
+  // the block's P^T as two bf16 B operands.  Lane value e holds key
+  // t0 + 4*hf + 8*(e/4) + e%4, i.e. bit 8*(e/4) + e%4 of a 32-bit word whose
+  // bit i is key t0 + 4*hf + i.
+  auto softmax = [&](floatx16 &sv, const int t0, bf16x8 (&pb)[2]) {
+    if (t0 + 32 > mask_from) {
+      const int base = t0 + 4 * hf;
+      const int room = t_end - base;  // keys inside the slot
+      const int pre = c - base;       // prefix keys (always visible)
+      uint32_t keep = pre <= 0 ? 0u : pre >= 32 ? ~0u : ((1u << pre) - 1u);
+      if (tree) {
+        const int sh = -pre;  // draft node of bit 0
+        keep |= sh >= 64 || sh <= -32 ? 0u
+                : sh >= 0         ? static_cast<uint32_t>(anc_q >> sh)
+                                  : static_cast<uint32_t>(anc_q << (-sh));
+      }
+      keep &= room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int bit = 8 * (e >> 2) + (e & 3);
@@ -248,13 +315,19 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     // kSumLimit (a key well above the reference) or nothing is visible yet,
     // the wave takes the slow path: block maximum, new reference, rescale.
     // The normalised result does not depend on the reference.
-    float pv[16];
+    float p[16];
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      pv[e] = fast_exp2(fmaf(sv[e], cs, -m_run));
-      sum += pv[e];
+      p[e] = fast_exp2(fmaf(sv[e], cs, -m_run));
+      sum += p[e];
     }
+    to_bf16(p, pb);
+    // Keep the conversion ahead of the branch: otherwise the compiler sinks
+    // it into the fast path, the fp32 p stays live across the join with the
+    // slow path, and the merge copies the accumulators into new registers
+    // (spills, whose scratch loads would also wait on the DMA in flight).
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
     if (__builtin_expect(__any(!(sum <= kSumLimit) || m_run == kNegInf), 0)) {
       float mx = kNegInf;
 #pragma unroll
@@ -266,9 +339,10 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
       sum = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        pv[e] = fast_exp2(fmaf(sv[e], cs, -m_use));
-        sum += pv[e];
+        p[e] = fast_exp2(fmaf(sv[e], cs, -m_use));
+        sum += p[e];
       }
+      to_bf16(p, pb);
       if (__any(m_run != kNegInf && alpha != 1.f)) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
@@ -277,79 +351,40 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
       m_run = m_new;
     }
     l_run += sum;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      floatx8 x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = pv[8 * half + e];
-      pb[half] = __builtin_convertvector(x, bf16x8);
-    }
   };
 
-  // O^T += V^T . P^T for key block kb of the tile in stage `st`; V^T
-  // operands come from transpose reads (two per operand), all read first.
-  auto pv = [&](lds_char *const st, const int kb, const bf16x8 (&pb)[2]) {
-    bf16x4 va[4][2][2];
+  // O^T += V^T . P^T for one key block.
+  auto pv = [&](const bf16x8 (&va)[4][2], const bf16x8 (&pb)[2]) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        lds_char *vp = st + v_base + (kb * 2 + half) * 4096 + db * 1024;
-        va[db][half][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp));
-        va[db][half][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp + 512));
-      }
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const bf16x8 a = __builtin_shufflevector(va[db][half][0], va[db][half][1], 0, 1, 2, 3, 4,
-                                                 5, 6, 7);
-        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[half], o_acc[db], 0, 0, 0);
-      }
+      for (int half = 0; half < 2; ++half)
+        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][half], pb[half], o_acc[db], 0,
+                                                            0, 0);
   };
 
-  // The two waves sharing a SIMD (w and w + 4) run half a tile apart: the
-  // lagging half finishes the previous tile's second key block (softmax on
-  // the VALU, then P.V) while the leading half starts the new tile with its
-  // QK^T MFMAs, so one wave's VALU work overlaps the other's matrix work
-  // instead of both alternating in lock-step after every barrier.  The
-  // prefetch distance is two tiles, so the previous tile's stage is still
-  // intact while the lagging waves read it.
-  const bool lag = wave >= kNW / 2;
-  floatx16 s_keep = floatx16{};
-  int nv_keep = 0;
+  // Key block kb of the tile in stage st: V reads first (their latency
+  // overlaps the softmax), then softmax, then P.V.
+  auto block = [&](lds_char *const st, floatx16 &sv, const int kb, const int t0) {
+    bf16x8 va[4][2];
+    read_v(st, kb, va);
+    bf16x8 pb[2];
+    softmax(sv, t0, pb);
+    pv(va, pb);
+  };
+
+  // Tile j sits in stage j % kStages while tiles j+1 .. j+kAhead are in
+  // flight.  The barrier at the top of iteration j also tells every wave that
+  // the others are done with tile j-1, whose stage tile j+kAhead may reuse.
   for (int j = 0; j < n_tiles; ++j) {
-    wait_tile_and_sync(j + 1 < n_tiles);
-    if (j + 2 < n_tiles)
-      issue_tile(kc, vc, row_off + t_begin + (j + 2) * kTK, row_last, lane, wave,
-                 lds + ((j + 2) % kStages) * kStageBytes);
+    wait_tile_and_sync(min(n_tiles - 1 - j, kAhead - 1));
+    if (j + kAhead < n_tiles) issue_tile(j + kAhead);
     lds_char *const st = lds + (j % kStages) * kStageBytes;
-    const int nv = min(kTK, t_end - (t_begin + j * kTK));
-    if (lag && j > 0) {
-      bf16x8 pb[2];
-      softmax(s_keep, 32, nv_keep, pb);
-      pv(lds + ((j - 1) % kStages) * kStageBytes, 1, pb);
-    }
+    const int t0 = t_begin + j * kTK;
     floatx16 sv[2];
     qk(st, sv);
-    {
-      bf16x8 pb[2];
-      softmax(sv[0], 0, nv, pb);
-      pv(st, 0, pb);
-    }
-    if (lag) {
-      s_keep = sv[1];
-      nv_keep = nv;
-    } else {
-      bf16x8 pb[2];
-      softmax(sv[1], 32, nv, pb);
-      pv(st, 1, pb);
-    }
-  }
-  if (lag) {
-    bf16x8 pb[2];
-    softmax(s_keep, 32, nv_keep, pb);
-    pv(lds + ((n_tiles - 1) % kStages) * kStageBytes, 1, pb);
+    block(st, sv[0], 0, t0);
+    block(st, sv[1], 1, t0 + 32);
   }
 
   // ---- epilogue --------------------------------------------------------------
@@ -360,9 +395,8 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (hf == 0 && r < P.R)
     P.lse_part[prow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
-  constexpr int kRowStride = kEpiRowStride;
   __syncthreads();  // every wave is done with the K/V stages
-  char *ep = smem + wave * 32 * kRowStride;
+  char *ep = smem + wave * 32 * kEpiRowStride;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -372,7 +406,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
       v4.y = o_acc[db][4 * jj + 1] * inv;
       v4.z = o_acc[db][4 * jj + 2] * inv;
       v4.w = o_acc[db][4 * jj + 3] * inv;
-      *reinterpret_cast<float4 *>(ep + l32 * kRowStride + (32 * db + 8 * jj + 4 * hf) * 4) = v4;
+      *reinterpret_cast<float4 *>(ep + l32 * kEpiRowStride + (32 * db + 8 * jj + 4 * hf) * 4) = v4;
     }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -380,9 +414,8 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int row = 2 * it + (lane >> 5);  // two rows per instruction
-    const float4 v4 = *reinterpret_cast<const float4 *>(ep + row * kRowStride + (lane & 31) * 16);
-    if (row_base + row < P.R)
-      *reinterpret_cast<float4 *>(dst0 + row * kD + (lane & 31) * 4) = v4;
+    const float4 v4 = *reinterpret_cast<const float4 *>(ep + row * kEpiRowStride + (lane & 31) * 16);
+    if (row_base + row < P.R) *reinterpret_cast<float4 *>(dst0 + row * kD + (lane & 31) * 4) = v4;
   }
 }
 

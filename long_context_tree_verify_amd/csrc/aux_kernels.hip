@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void validate_kernel(Plan P) {
   int32_t bits = 0;
   if (threadIdx.x == 0 && (c < 0 || c > P.max_ctx || static_cast<int64_t>(c) + P.N > P.cap))
     bits |= kErrCtx;
-  if (P.parent && P.tree_slot >= 0)
+  if (P.parent && P.has_tree)
     for (int i = threadIdx.x; i < P.N; i += blockDim.x) {
       const int p = P.parent[static_cast<int64_t>(b) * P.N + i];
       if (p < -1 || p >= i) bits |= kErrParent;

@@ -99,6 +99,40 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
     p->row_chunks = 1;
   }
 
+  p->has_prefix = with_prefix;
+  p->has_tree = with_tree;
+  p->unified = p->kernel == kKernDma256;
+  if (p->unified) {
+    // One key range per (b, kv head): prefix then draft rows.  One workgroup
+    // per CU: as many splits as fit in one round of the CUs (splits of a
+    // multiple of 32 keys), more only when the batch is ragged and a split
+    // would exceed 64 tiles.
+    const int64_t keys = (with_prefix ? d->max_ctx : 0) + (with_tree ? d->n_draft : 0);
+    const int64_t units = static_cast<int64_t>(p->B) * p->Hkv * p->row_chunks;
+    int64_t target;
+    if (d->num_splits > 0) {
+      target = d->num_splits;
+    } else {
+      target = std::max<int64_t>(1, kPlanCUs / units);
+      if (p->B > 1)
+        while (ceil_div(keys, target * tile) > 64 && target * 2 <= kMaxSplits) target *= 2;
+    }
+    target = std::max<int64_t>(1, std::min<int64_t>(target, kMaxSplits));
+    const int64_t kps = std::max<int64_t>(32, ceil_div(ceil_div(keys, target), 32) * 32);
+    p->keys_per_split = static_cast<int32_t>(kps);
+    p->n_splits = keys > 0 ? static_cast<int32_t>(ceil_div(keys, kps)) : 0;
+    p->tree_slot = -1;
+    p->n_slots = p->n_splits;
+    p->n_parts = p->n_slots * p->kgroups;
+    const size_t rows = static_cast<size_t>(p->n_parts) * p->B * p->Hkv * p->R;
+    size_t off = 0;
+    off += align_up(rows * p->D * sizeof(float));  // o_part
+    off += align_up(rows * sizeof(float));         // lse_part
+    off += kAlign;                                 // error word
+    *ws_bytes = off;
+    return HSV_OK;
+  }
+
   const int64_t keys = sparse ? d->n_sel : d->max_ctx;
   if (with_prefix && keys > 0) {
     int64_t target;
@@ -156,7 +190,7 @@ hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, cons
   size_t need = 0;
   hsv_status st = make_plan(d, sparse, &p, &need);
   if (st != HSV_OK) return st;
-  const bool with_tree = p.tree_slot >= 0;
+  const bool with_tree = p.has_tree;
   if (!q || !k || !v || !ctx_lens || !o || !lse) return HSV_ERR_NULL;
   if (sparse && !kv_idx) return HSV_ERR_NULL;
   if (with_tree && ((parent == nullptr) == (anc == nullptr))) return HSV_ERR_NULL;

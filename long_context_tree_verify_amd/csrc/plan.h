@@ -19,10 +19,14 @@ enum : int {
 
 // One verify call, resolved on the host.  Grouped row r of KV head g is
 // (node i, query head g*G + hh) with r = i*G + hh; a KV head owns R = G*N
-// query rows.  Keys are cut into "slots": slots [0, n_splits) are contiguous
-// ranges of the prefix (keys_per_split each), slot tree_slot (if >= 0) is the
-// draft block under the ancestor mask.  A workgroup of slot s writes
-// kgroups partial results, parts s*kgroups .. s*kgroups + kgroups-1.
+// query rows.  Keys are cut into "slots".  Separate layout (unified == 0):
+// slots [0, n_splits) are contiguous ranges of the prefix (keys_per_split
+// each), slot tree_slot (if >= 0) is the draft block under the ancestor mask.
+// Unified layout (unified == 1): the prefix rows [0, c) and the draft rows
+// [c, c+N) that follow them in the cache form one key range, cut into
+// n_splits slots of keys_per_split keys; keys at or past c are masked by the
+// ancestor bits.  A workgroup of slot s writes kgroups partial results, parts
+// s*kgroups .. s*kgroups + kgroups-1.
 struct Plan {
   // inputs
   const void *q;
@@ -47,7 +51,10 @@ struct Plan {
   int32_t kernel;           // kKern*
   int32_t n_splits;         // prefix slots (0 when the prefix is left out)
   int32_t keys_per_split;   // multiple of the kernel's key tile
-  int32_t tree_slot;        // slot index of the tree part, or -1
+  int32_t has_prefix;       // the prefix part is included
+  int32_t has_tree;         // the draft (tree) part is included
+  int32_t unified;          // slot layout (see above)
+  int32_t tree_slot;        // slot index of the tree part (separate layout), or -1
   int32_t n_slots;          // n_splits + (tree_slot >= 0)
   int32_t kgroups;          // partial results per slot workgroup
   int32_t n_parts;          // n_slots * kgroups
