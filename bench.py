@@ -9,10 +9,17 @@ Several copies of the KV cache (standing for the caches of successive
 layers) are rotated so that a step never finds its cache in the 256 MB
 Infinity Cache left over from the previous step.
 
+The K timed steps are issued two ways: one Python call per step, and replayed
+from one captured HIP graph (no host work between kernels); each is K whole
+steps between synchronisations, and the faster is the step time.
+
 Prints ONE JSON line (rank 0):
-  value = KV-read GB/s of the whole step; ms_per_step = wall time per step;
-  roofline = the dominant kernel (prefix/tree partials) timed with HIP events
-  on its own stream; cpu_baseline = the fp64 oracle on a bounded row sample.
+  value = KV-read GB/s of the whole step; ms_per_step = time per step;
+  roofline = the dominant kernel (the attention partials), its average
+  duration from HIP events around a graph of K back-to-back launches on its
+  stream; traffic = its HBM bytes per launch from the committed rocprofv3
+  counter summary, when that summary was taken on the current kernel source;
+  cpu_baseline = the fp64 oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -34,6 +41,12 @@ METRIC = "verify-step µs and KV-read GB/s (% HBM peak) at 32k ctx, 64-node tree
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 INFINITY_CACHE_BYTES = 256 * 2 ** 20
+# Counter summary of the dominant kernel (written from rocprofv3 --pmc runs)
+# and the sources whose hash it records.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_partial_dma_tree32k_counters.md")
+KERNEL_SOURCES = ("long_context_tree_verify_amd/csrc/attn_dma.hip",
+                  "long_context_tree_verify_amd/csrc/common.hpp",
+                  "long_context_tree_verify_amd/csrc/plan.h")
 
 
 def log(msg):
@@ -58,6 +71,35 @@ def step_flops(inp) -> int:
     per_key_row = 2 * 2 * wl.head_dim * wl.group * wl.n_draft   # per key per kv head
     row = 2 * wl.head_dim * (2 if wl.dtype == "bf16" else 4)
     return kv_bytes(inp) // row * per_key_row
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the partial kernel from the committed counter
+    summary, or None if there is none for this workload or the kernel source
+    changed since it was taken."""
+    if workload != "tree32k" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(inp, target_s: float):
@@ -85,12 +127,19 @@ def cpu_baseline(inp, target_s: float):
         n2 = min(total, max(n + 1, int(n * target_s / max(t, 1e-3))))
         t = run(n2)
         n = n2
-    step_s = t * total / n
+    reps = 1
+    if n == total:  # the whole step fits: repeat it for a stable figure
+        while t < target_s:
+            t += run(n)
+            reps += 1
+    step_s = t / reps * total / n
     gbs = kv_bytes(inp) / step_s / 1e9
+    what = (f"{n} of {total}" if n < total else f"all {total}") + \
+        f" (b, node, head) rows of the {wl.name} step, each over its full key set, fp64"
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {total} (b, node, head) rows of the {wl.name} step, each over "
-                      f"its full key set, fp64; {t:.2f} s measured, scaled by {total}/{n}",
-            "step_s": round(step_s, 3)}
+            "sample": f"{what}; {reps} run(s), {t:.2f} s measured"
+                      + (f", scaled by {total}/{n}" if n < total else ""),
+            "step_s": round(step_s, 4)}
 
 
 def main(argv=None) -> int:
@@ -154,11 +203,11 @@ def main(argv=None) -> int:
                          out_dtype=hsv.HSV_BF16 if out_dtype == torch.bfloat16 else hsv.HSV_F32,
                          num_splits=args.num_splits)
     ws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
 
     def call(j, flags=0):
+        # stream=None: torch's current stream (the capture stream inside a graph)
         kw = dict(max_ctx=max_ctx, out_dtype=out_dtype, num_splits=args.num_splits,
-                  flags=flags, o=o, lse=lse, workspace=ws, stream=stream)
+                  flags=flags, o=o, lse=lse, workspace=ws, stream=None)
         c = j % copies
         if kv_idx is None:
             hsv.hsv_verify_attn(q, ks[c], vs[c], ctx, parent, **kw)
@@ -170,30 +219,48 @@ def main(argv=None) -> int:
         call(j)
     torch.cuda.synchronize()
 
-    # timed region: K whole steps; the partial-attention phase (the dominant
-    # kernel) is bracketed by events on the stream it runs on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for j in range(args.steps):
-        ev[j][0].record(stream)
-        call(j, hsv.HSV_FLAG_PHASE_PARTIALS)
-        ev[j][1].record(stream)
-        call(j, hsv.HSV_FLAG_PHASE_MERGE)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
-
-    # the same steps without events, each call both phases (the product call)
-    torch.cuda.synchronize()
+    # K steps issued one Python call at a time (reported alongside)
     t2 = time.perf_counter()
     for j in range(args.steps):
         call(j)
     torch.cuda.synchronize()
-    plain_ms = (time.perf_counter() - t2) * 1e3 / args.steps
-    ms = min(wall_ms, plain_ms)
+    eager_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+
+    # The K timed steps as one captured graph (steps j = 0..K-1, cache copy
+    # j % copies), replayed once untimed, then once timed.
+    side = torch.cuda.Stream(dev)
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step, stream=side):
+        for j in range(args.steps):
+            call(j)
+    g_step.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    g_step.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    graph_ms = ev0.elapsed_time(ev1) / args.steps
+    # Both are whole-job times of the same K steps; report the faster issue mode.
+    ms = min(wall_ms, eager_ms)
+
+    # The dominant kernel alone: K back-to-back launches of the partial phase
+    # in one graph; HIP events on the stream it runs on bracket the replay.
+    g_part = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_part, stream=side):
+        for j in range(args.steps):
+            call(j, hsv.HSV_FLAG_PHASE_PARTIALS)
+    g_part.replay()
+    torch.cuda.synchronize()
+    ek0, ek1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ek0.record()
+    g_part.replay()
+    ek1.record()
+    torch.cuda.synchronize()
+    kern_ms = ek0.elapsed_time(ek1) / args.steps
 
     if args.copy_probe:
         src = torch.empty(2 ** 26, dtype=torch.float32, device=dev).fill_(1.0)
@@ -204,6 +271,13 @@ def main(argv=None) -> int:
 
     nbytes = kv_bytes(inp)
     flops = step_flops(inp)
+    traffic = recorded_traffic(wl.name) if kv_idx is None and bf else None
+    if not bf:
+        kernel_name = "attn_partial_valu"
+    elif kv_idx is None and wl.head_dim == 128 and wl.group * wl.n_draft > 128:
+        kernel_name = "attn_partial_dma (prefix + draft rows, split along keys)"
+    else:
+        kernel_name = "attn_partial_mfma (prefix or index-set splits, draft slot)"
     gbs = nbytes / (ms * 1e-3) / 1e9
     kern_gbs = nbytes / (kern_ms * 1e-3) / 1e9
     result = {
@@ -228,12 +302,17 @@ def main(argv=None) -> int:
                    "kv_read_bytes": nbytes, "flop": flops, "cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "attention partials (prefix splits + tree)",
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": kernel_name,
                      "kernel_us": round(kern_ms * 1e3, 2),
                      "mfma_util": round(flops / (kern_ms * 1e-3) / 1e12 /
                                         MFMA_BF16_PEAK_TFLOPS, 4)},
-        "timing": {"wall_ms_with_phase_events": round(wall_ms, 5),
-                   "wall_ms_plain": round(plain_ms, 5)},
+        "timing": {"graph_ms_per_step_wall": round(wall_ms, 5),
+                   "graph_ms_per_step_events": round(graph_ms, 5),
+                   "eager_ms_per_step": round(eager_ms, 5)},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on a row sample")

@@ -247,3 +247,51 @@ def test_validate_flag(hsv, gpu):
         run_hip(hsv, sp, sdev2, flags=hsv.HSV_FLAG_VALIDATE)
     assert e.value.code == hsv.HSV_ERR_DEVICE_CHECK
     torch.cuda.synchronize()
+
+
+def test_graph_replays_match_eager(hsv, gpu):
+    """A captured call replayed several times, with eager calls and
+    synchronisations in between, gives the eager result bit for bit each time
+    (the benchmark times graph replays)."""
+    import torch
+    for wl, over in (("tree32k", (("ctx", (3000, 3000)),)),
+                     ("chain_b16", (("ctx", (700, 2000)), ("batch", 3))),
+                     ("sparse64k", SPARSE_CASES[1])):
+        inp = cached_inputs(wl, over, poison=wl == "sparse64k")
+        log(f"graph replay case {wl} {dict(over)}")
+        dev = device_inputs(inp, gpu)
+        o_ref, l_ref = run_hip(hsv, inp, dev)
+        o = torch.empty_like(o_ref)
+        lse = torch.empty_like(l_ref)
+        max_ctx = int(inp.ctx_lens.max())
+        sparse = inp.kv_idx is not None
+        n = hsv.hsv_verify_workspace_bytes(hsv.make_desc(
+            batch=inp.wl.batch, n_draft=inp.wl.n_draft, n_q_heads=inp.wl.n_q_heads,
+            n_kv_heads=inp.wl.n_kv_heads, head_dim=inp.wl.head_dim,
+            kv_capacity=inp.k.shape[2], max_ctx=max_ctx,
+            n_sel=inp.kv_idx.shape[2] if sparse else 0,
+            in_dtype=hsv.HSV_BF16 if inp.is_bf16 else hsv.HSV_F32, out_dtype=hsv.HSV_F32))
+        ws = torch.empty(n, dtype=torch.uint8, device=gpu)
+
+        def call():
+            kw = dict(max_ctx=max_ctx, out_dtype=torch.float32, o=o, lse=lse, workspace=ws)
+            if sparse:
+                hsv.hsv_verify_attn_sparse(dev["q"], dev["k"], dev["v"], dev["ctx"],
+                                           dev["parent"], None, dev["kv_idx"], **kw)
+            else:
+                hsv.hsv_verify_attn(dev["q"], dev["k"], dev["v"], dev["ctx"], dev["parent"],
+                                    None, **kw)
+
+        side = torch.cuda.Stream(gpu)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            call()
+        for rep in range(3):
+            o.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {rep}"
+            o2, l2 = run_hip(hsv, inp, dev)      # eager work between replays
+            assert torch.equal(o2, o_ref) and torch.equal(l2, l_ref)
