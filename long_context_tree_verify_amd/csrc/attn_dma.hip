@@ -48,6 +48,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -61,12 +63,14 @@ constexpr int kTileBytes = kTK * kRowBytes;    // 16 KB (K or V)
 constexpr int kStageBytes = 2 * kTileBytes;    // K then V
 constexpr int kStages = 4;
 constexpr int kAhead = 2;           // tiles in flight beyond the one computed on
-static_assert(kAhead + 1 <= kStages, "the stage refilled was read one iteration earlier");
+// The DMA of tile j+1+kAhead is issued while block 2j+1 (tile j) is still
+// being computed, so its stage must differ from those of tiles j and j+1.
+static_assert(kAhead + 2 <= kStages, "stage of the refilled tile is still being read");
 constexpr int kBlocks = kTileBytes / 1024;     // 1 KB DMA blocks per K (or V) tile
 constexpr int kBlocksPerWave = kBlocks / kNW;  // per wave, for K and again for V
 constexpr int kDmaPerTile = 2 * kBlocksPerWave;  // DMA instructions per thread per tile
-// Epilogue staging: every wave's 32 x 128 fp32 partial, rows padded by 16 B.
-constexpr int kEpiRowStride = kD * 4 + 16;
+// Epilogue staging: every wave's 32 x 128 fp16 partial, rows padded by 16 B.
+constexpr int kEpiRowStride = kD * 2 + 16;
 constexpr int kSmemBytes = kStages * kStageBytes > kNW * 32 * kEpiRowStride
                                ? kStages * kStageBytes
                                : kNW * 32 * kEpiRowStride;
@@ -144,7 +148,10 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   const int64_t prow = (static_cast<int64_t>(part) * BH + bg) * P.R + r;
 
   if (n_tiles == 0) {
-    if (r < P.R && hf == 0) P.lse_part[prow] = kNegInf;
+    if (r < P.R && hf == 0) {
+      P.lse_part[prow] = kNegInf;
+      P.o_scale[prow] = 1.f;
+    }
     return;
   }
 
@@ -243,19 +250,16 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   float m_run = kNegInf, l_run = 0.f;
   const float cs = P.scale_log2;
 
-  // S^T = K . Q^T for the two 32-key blocks of the tile in stage `st`.
-  auto qk = [&](lds_char *const st, floatx16 (&sv)[2]) {
+  // S^T = K . Q^T for one 32-key block (block kb of the tile in stage st).
+  auto qk_block = [&](lds_char *const st, const int kb, floatx16 &sv) {
+    bf16x8 ka[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 ka[8];
+    for (int ks = 0; ks < 8; ++ks)
+      ka[ks] = *(const lds_bf16x8 *)(st + k_base + kb * 8192 + (ks >> 1) * 1024 + (ks & 1) * 512);
+    sv = floatx16{};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        ka[ks] = *(const lds_bf16x8 *)(st + k_base + kb * 8192 + (ks >> 1) * 1024 + (ks & 1) * 512);
-      sv[kb] = floatx16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sv[kb], 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sv, 0, 0, 0);
   };
 
   // V^T operands of key block kb (two transpose reads per operand).
@@ -287,34 +291,32 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     }
   };
 
-  // Mask and softmax of one 32-key block (cache rows t0 .. t0+31); returns
-  // the block's P^T as two bf16 B operands.  Lane value e holds key
-  // t0 + 4*hf + 8*(e/4) + e%4, i.e. bit 8*(e/4) + e%4 of a 32-bit word whose
-  // bit i is key t0 + 4*hf + i.
-  auto softmax = [&](floatx16 &sv, const int t0, bf16x8 (&pb)[2]) {
-    if (t0 + 32 > mask_from) {
-      const int base = t0 + 4 * hf;
-      const int room = t_end - base;  // keys inside the slot
-      const int pre = c - base;       // prefix keys (always visible)
-      uint32_t keep = pre <= 0 ? 0u : pre >= 32 ? ~0u : ((1u << pre) - 1u);
-      if (tree) {
-        const int sh = -pre;  // draft node of bit 0
-        keep |= sh >= 64 || sh <= -32 ? 0u
-                : sh >= 0         ? static_cast<uint32_t>(anc_q >> sh)
-                                  : static_cast<uint32_t>(anc_q << (-sh));
-      }
-      keep &= room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int bit = 8 * (e >> 2) + (e & 3);
-        sv[e] = ((keep >> bit) & 1u) ? sv[e] : kNegInf;
-      }
+  // Mask of one 32-key block (cache rows t0 .. t0+31).  Lane value e holds
+  // key t0 + 4*hf + 8*(e/4) + e%4, i.e. bit 8*(e/4) + e%4 of a 32-bit word
+  // whose bit i is key t0 + 4*hf + i.
+  auto apply_mask = [&](floatx16 &sv, const int t0) {
+    const int base = t0 + 4 * hf;
+    const int room = t_end - base;  // keys inside the slot
+    const int pre = c - base;       // prefix keys (always visible)
+    uint32_t keep = pre <= 0 ? 0u : pre >= 32 ? ~0u : ((1u << pre) - 1u);
+    if (tree) {
+      const int sh = -pre;  // draft node of bit 0
+      keep |= sh >= 64 || sh <= -32 ? 0u
+              : sh >= 0         ? static_cast<uint32_t>(anc_q >> sh)
+                                : static_cast<uint32_t>(anc_q << (-sh));
     }
-    // Probabilities against the running reference m_run (log2 domain).
-    // Fast path: no block maximum; if the lane's 16 probabilities sum above
-    // kSumLimit (a key well above the reference) or nothing is visible yet,
-    // the wave takes the slow path: block maximum, new reference, rescale.
-    // The normalised result does not depend on the reference.
+    keep &= room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int bit = 8 * (e >> 2) + (e & 3);
+      sv[e] = ((keep >> bit) & 1u) ? sv[e] : kNegInf;
+    }
+  };
+
+  // Probabilities of one block against the running reference m_run (log2
+  // domain), as bf16 B operands, and their exact fp32 sum.  No branches: this
+  // is the work that overlaps the next block's QK^T MFMAs.
+  auto fast_p = [&](const floatx16 &sv, bf16x8 (&pb)[2]) {
     float p[16];
     float sum = 0.f;
 #pragma unroll
@@ -323,34 +325,36 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
       sum += p[e];
     }
     to_bf16(p, pb);
-    // Keep the conversion ahead of the branch: otherwise the compiler sinks
-    // it into the fast path, the fp32 p stays live across the join with the
-    // slow path, and the merge copies the accumulators into new registers
-    // (spills, whose scratch loads would also wait on the DMA in flight).
-    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
-    if (__builtin_expect(__any(!(sum <= kSumLimit) || m_run == kNegInf), 0)) {
-      float mx = kNegInf;
+    return sum;
+  };
+
+  // Slow path of the softmax: the block maximum becomes the new reference,
+  // the accumulators are rescaled and the block's probabilities recomputed.
+  // Taken when a lane's 16 probabilities sum above kSumLimit (a key well
+  // above the reference) or nothing has been visible yet.  The normalised
+  // result does not depend on the reference.
+  auto slow_p = [&](const floatx16 &sv, bf16x8 (&pb)[2], float &sum) {
+    float mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * cs;
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);  // 0 when m_run = -inf
-      sum = 0.f;
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * cs;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);  // 0 when m_run = -inf
+    float p[16];
+    sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = fast_exp2(fmaf(sv[e], cs, -m_use));
-        sum += p[e];
-      }
-      to_bf16(p, pb);
-      if (__any(m_run != kNegInf && alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
-      }
-      l_run *= alpha;
-      m_run = m_new;
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(fmaf(sv[e], cs, -m_use));
+      sum += p[e];
     }
-    l_run += sum;
+    to_bf16(p, pb);
+    if (__any(m_run != kNegInf && alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
+    }
+    l_run *= alpha;
+    m_run = m_new;
   };
 
   // O^T += V^T . P^T for one key block.
@@ -363,64 +367,99 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
                                                             0, 0);
   };
 
-  // Key block kb of the tile in stage st: V reads first (their latency
-  // overlaps the softmax), then softmax, then P.V.
-  auto block = [&](lds_char *const st, floatx16 &sv, const int kb, const int t0) {
+  // Software pipeline over 32-key blocks t = 0 .. 2*n_tiles - 1 (block t is
+  // half t % 2 of tile t / 2).  Step t issues the QK^T MFMAs of block t+1
+  // in the same branch-free stretch as block t's exponentials, so the matrix
+  // cores and the VALU work side by side within one wave; then block t's
+  // slow-path check and its P.V.  Tile j sits in stage j % kStages; the
+  // barrier before the first block of tile j+1 (at step 2j+1) also tells
+  // every wave that the others are done with tile j-1, whose stage the DMA
+  // of tile j+1+kAhead then reuses.  The last step's "next block" reads a
+  // stage that holds an older tile: its scores are never used.
+  const int n_blocks = 2 * n_tiles;
+  wait_tile_and_sync(min(n_tiles - 1, kAhead - 1));
+  if (kAhead < n_tiles) issue_tile(kAhead);
+  floatx16 s_cur;
+  qk_block(lds, 0, s_cur);
+  for (int t = 0; t < n_blocks; ++t) {
+    const int j = t >> 1, kb = t & 1;
+    lds_char *const st = lds + (j % kStages) * kStageBytes;
+    const int t0 = t_begin + t * 32;
+    if (kb == 1 && t + 1 < n_blocks) {
+      wait_tile_and_sync(min(n_tiles - 2 - j, kAhead - 1));
+      if (j + 1 + kAhead < n_tiles) issue_tile(j + 1 + kAhead);
+    }
+    if (t0 + 32 > mask_from) apply_mask(s_cur, t0);
     bf16x8 va[4][2];
     read_v(st, kb, va);
+    floatx16 s_nxt;
     bf16x8 pb[2];
-    softmax(sv, t0, pb);
+    qk_block(lds + (((t + 1) >> 1) % kStages) * kStageBytes, (t + 1) & 1, s_nxt);
+    float sum = fast_p(s_cur, pb);
+    // Keep the conversion ahead of the branch: otherwise the compiler sinks
+    // it into the fast path, the fp32 probabilities stay live across the
+    // join with the slow path, and the merge copies the accumulators into
+    // new registers (spills, whose scratch loads would also wait on the DMA
+    // in flight).
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
+    if (__builtin_expect(__any(!(sum <= kSumLimit) || m_run == kNegInf), 0))
+      slow_p(s_cur, pb, sum);
+    l_run += sum;
     pv(va, pb);
-  };
-
-  // Tile j sits in stage j % kStages while tiles j+1 .. j+kAhead are in
-  // flight.  The barrier at the top of iteration j also tells every wave that
-  // the others are done with tile j-1, whose stage tile j+kAhead may reuse.
-  for (int j = 0; j < n_tiles; ++j) {
-    wait_tile_and_sync(min(n_tiles - 1 - j, kAhead - 1));
-    if (j + kAhead < n_tiles) issue_tile(j + kAhead);
-    lds_char *const st = lds + (j % kStages) * kStageBytes;
-    const int t0 = t_begin + j * kTK;
-    floatx16 sv[2];
-    qk(st, sv);
-    block(st, sv[0], 0, t0);
-    block(st, sv[1], 1, t0 + 32);
+    s_cur = s_nxt;
   }
 
   // ---- epilogue --------------------------------------------------------------
-  // Normalise, then write the wave's 32 x 128 partial through LDS so that the
-  // global stores are whole 512-byte rows (lane l holds a query column; rows
-  // are padded by 16 bytes so the column-wise LDS writes spread over banks).
+  // The normalised partial row of a query is written as fp16 scaled by a
+  // power of two: its largest |value| lands in [0.5, 1), the scale 2^e goes
+  // to o_scale (exact), and every value keeps 11 significant bits -- half
+  // the bytes of fp32 for the write here and the merge's read.  The rows are
+  // staged through LDS (lane l holds a query column; rows padded by 16 bytes
+  // so the column-wise writes spread over banks) so the global stores are
+  // whole 256-byte rows.
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (hf == 0 && r < P.R)
+  float amax = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o_acc[db][e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave)) * inv;
+  int ex = 0;
+  if (amax > 0.f && amax < __builtin_huge_valf()) (void)frexpf(amax, &ex);
+  const float mul = ldexpf(inv, -ex);
+  if (hf == 0 && r < P.R) {
     P.lse_part[prow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    P.o_scale[prow] = ldexpf(1.f, ex);
+  }
   __syncthreads();  // every wave is done with the K/V stages
   char *ep = smem + wave * 32 * kEpiRowStride;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      float4 v4;
-      v4.x = o_acc[db][4 * jj + 0] * inv;
-      v4.y = o_acc[db][4 * jj + 1] * inv;
-      v4.z = o_acc[db][4 * jj + 2] * inv;
-      v4.w = o_acc[db][4 * jj + 3] * inv;
-      *reinterpret_cast<float4 *>(ep + l32 * kEpiRowStride + (32 * db + 8 * jj + 4 * hf) * 4) = v4;
+      floatx4 v4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v4[q] = o_acc[db][4 * jj + q] * mul;
+      *reinterpret_cast<halfx4 *>(ep + l32 * kEpiRowStride + (32 * db + 8 * jj + 4 * hf) * 2) =
+          __builtin_convertvector(v4, halfx4);
     }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  float *dst0 = P.o_part + (prow - l32) * kD;  // row row_base of this wave
+  // row row_base of this wave, fp16
+  char *dst0 = reinterpret_cast<char *>(P.o_part) + (prow - l32) * kD * 2;
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int row = 2 * it + (lane >> 5);  // two rows per instruction
-    const float4 v4 = *reinterpret_cast<const float4 *>(ep + row * kEpiRowStride + (lane & 31) * 16);
-    if (row_base + row < P.R) *reinterpret_cast<float4 *>(dst0 + row * kD + (lane & 31) * 4) = v4;
+  for (int it = 0; it < 8; ++it) {
+    const int row = 4 * it + (lane >> 4);  // four rows per instruction
+    const uint4 v = *reinterpret_cast<const uint4 *>(ep + row * kEpiRowStride + (lane & 15) * 16);
+    if (row_base + row < P.R)
+      *reinterpret_cast<uint4 *>(dst0 + row * kD * 2 + (lane & 15) * 16) = v;
   }
 }
 
 }  // namespace
 
+// The kernel writes its partials in the scaled fp16 format (part_f16).
 bool dma_supports(const Plan &p) {
   return p.in_dtype == kBF16 && p.D == kD && p.n_sel == 0 && p.R > 128;
 }

@@ -22,79 +22,135 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t *parent, ui
 
 // --------------------------------------------------------------------------
 // Log-sum-exp merge (LongSpec section 2.C: exact combination of the parts).
-// One wave per output row; lane l owns features 2l, 2l+1 (D = 128) or l
-// (D = 64).  Lane p reads part p's LSE, the wave reduces them to
-// lse = m + log sum exp(lse_p - m), and the per-part weights exp(lse_p - lse)
-// are broadcast with v_readlane while eight parts' rows are in flight.
-// Parts with lse = -inf get weight 0 and their (possibly never written) o
-// rows are discarded by a select, so they cannot inject NaN.
+// One wave per output row.  A part's row of D floats is read by L = D/4
+// lanes (16 bytes each), so one load instruction covers S = 64/L parts;
+// lane l takes sub-group l / L and features 4*(l % L) .. +3.  All loads of a
+// group of 32 parts (and the LSE of every part) are issued before any is
+// used, so a row costs about one memory latency instead of one per batch.
+// lse = m + log sum_p exp(lse_p - m); O = sum_p exp(lse_p - lse) * O_p.
+// Parts with lse = -inf get weight 0 and their (possibly never written) rows
+// are discarded by a select, so they cannot inject NaN.  The S sub-group
+// sums are combined with cross-lane adds; lanes of sub-group 0 end up with
+// the row.  With F16 the part rows are fp16, each to be multiplied by its
+// power-of-two scale (o_scale), which is folded into the part's weight.
 // --------------------------------------------------------------------------
 constexpr int kMergeRowsPerBlock = 4;  // 256 threads, one wave per row
+constexpr int kMergeGroup = 32;        // parts whose rows are in flight together
 
-template <int D>
-__device__ __forceinline__ void merge_row(const float *o_parts, const float *lse_parts,
-                                          int n_parts, int64_t part_stride_rows, int64_t row,
-                                          int lane, float (&acc)[D / 64], float *lse_out) {
-  constexpr int DL = D / 64;
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+template <bool F16>
+__device__ __forceinline__ float4 load4(const void *base, int64_t elem) {
+  if constexpr (F16) {
+    const halfx4 h = *reinterpret_cast<const halfx4 *>(static_cast<const _Float16 *>(base) + elem);
+    return make_float4(static_cast<float>(h[0]), static_cast<float>(h[1]),
+                       static_cast<float>(h[2]), static_cast<float>(h[3]));
+  } else {
+    return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem);
+  }
+}
+
+template <int D, bool F16>
+__device__ __forceinline__ void merge_row(const void *o_parts, const float *lse_parts,
+                                          const float *o_scale, int n_parts,
+                                          int64_t part_stride_rows, int64_t row, int lane,
+                                          float4 *acc_out, float *lse_out) {
+  constexpr int L = D / 4;           // lanes per part row
+  constexpr int S = kWave / L;       // parts per load instruction
+  constexpr int U = kMergeGroup / S; // loads per lane per group
+  const int sub = lane / L, c = lane % L;
   const float *lp = lse_parts + row;
-  float m = kNegInf;
-  for (int p = lane; p < n_parts; p += kWave) m = fmaxf(m, lp[p * part_stride_rows]);
-  m = wave_max(m);
+  const float *sp = F16 ? o_scale + row : nullptr;
+  const int64_t o0 = row * D + 4 * c;
+  const int64_t ostride = part_stride_rows * D;
+
+  // first group's rows: in flight with the LSE loads
+  float4 v[U];
 #pragma unroll
-  for (int j = 0; j < DL; ++j) acc[j] = 0.f;
+  for (int u = 0; u < U; ++u) {
+    const int p = min(S * u + sub, n_parts - 1);  // stays in bounds
+    v[u] = load4<F16>(o_parts, o0 + p * ostride);
+  }
+  // LSEs: parts 0..63 in flight with the rows, the rest (if any) by a loop
+  const float l0 = lane < n_parts ? lp[static_cast<int64_t>(lane) * part_stride_rows] : kNegInf;
+  float m = l0;
+  for (int p = lane + kWave; p < n_parts; p += kWave) m = fmaxf(m, lp[p * part_stride_rows]);
+  m = wave_max(m);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (m == kNegInf) {
+    *acc_out = acc;
     *lse_out = kNegInf;
     return;
   }
-  float sum = 0.f;
-  for (int p = lane; p < n_parts; p += kWave)
+  float sum = fast_exp2((l0 - m) * kLog2e);  // -inf -> 0
+  for (int p = lane + kWave; p < n_parts; p += kWave)
     sum += fast_exp2((lp[p * part_stride_rows] - m) * kLog2e);
   sum = wave_sum(sum);
   const float lse = m + fast_log2(sum) * kLn2;
-  const float *op = o_parts + row * D + lane * DL;
-  const int64_t ostride = part_stride_rows * D;
-  constexpr int kBatch = 8;
-  for (int p0 = 0; p0 < n_parts; p0 += kWave) {
-    const int p = p0 + lane;
-    const float w_lane = p < n_parts ? fast_exp2((lp[p * part_stride_rows] - lse) * kLog2e) : 0.f;
-    const int n_here = min(kWave, n_parts - p0);
-    for (int u0 = 0; u0 < n_here; u0 += kBatch) {
-      float w[kBatch];
-      float v[kBatch][DL];
+
+  for (int p0 = 0; p0 < n_parts; p0 += kMergeGroup) {
+    if (p0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int q = min(p0 + u0 + u, n_parts - 1);  // stays in bounds
-        w[u] = u0 + u < n_here
-                   ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), u0 + u))
-                   : 0.f;
-#pragma unroll
-        for (int j = 0; j < DL; ++j) v[u][j] = op[q * ostride + j];
+      for (int u = 0; u < U; ++u) {
+        const int p = min(p0 + S * u + sub, n_parts - 1);
+        v[u] = load4<F16>(o_parts, o0 + p * ostride);
       }
+    }
+    // the LSE (and scale) of part p0 + j sits in lane base + j
+    float lsrc = l0;
+    int base = p0;
+    int psrc = lane;
+    if (p0 >= kWave) {
+      psrc = p0 + (lane & (kMergeGroup - 1));
+      lsrc = psrc < n_parts ? lp[psrc * part_stride_rows] : kNegInf;
+      base = 0;
+    }
+    float wsrc = fast_exp2((lsrc - lse) * kLog2e);
+    if constexpr (F16)
+      wsrc = lsrc > kNegInf ? wsrc * sp[min(psrc, n_parts - 1) * part_stride_rows] : 0.f;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
+    for (int u = 0; u < U; ++u) {
+      float w = 0.f;
 #pragma unroll
-        for (int j = 0; j < DL; ++j) acc[j] = fmaf(w[u], w[u] != 0.f ? v[u][j] : 0.f, acc[j]);
+      for (int q = 0; q < S; ++q) {
+        const float wq = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(wsrc), base + S * u + q));
+        w = sub == q ? wq : w;
+      }
+      const bool live = p0 + S * u + sub < n_parts && w != 0.f;
+      w = live ? w : 0.f;
+      acc.x = fmaf(w, live ? v[u].x : 0.f, acc.x);
+      acc.y = fmaf(w, live ? v[u].y : 0.f, acc.y);
+      acc.z = fmaf(w, live ? v[u].z : 0.f, acc.z);
+      acc.w = fmaf(w, live ? v[u].w : 0.f, acc.w);
     }
   }
+#pragma unroll
+  for (int off = L; off < kWave; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off, kWave);
+    acc.y += __shfl_xor(acc.y, off, kWave);
+    acc.z += __shfl_xor(acc.z, off, kWave);
+    acc.w += __shfl_xor(acc.w, off, kWave);
+  }
+  *acc_out = acc;
   *lse_out = lse;
 }
 
+// Lanes of sub-group 0 (lane < D/4) write features 4*lane .. 4*lane+3.
 template <int D>
-__device__ __forceinline__ void store_row(void *o, int out_dtype, int64_t base,
-                                          const float (&acc)[D / 64], int lane) {
-  constexpr int DL = D / 64;
+__device__ __forceinline__ void store_row(void *o, int out_dtype, int64_t base, float4 acc,
+                                          int lane) {
+  if (lane >= D / 4) return;
   if (out_dtype == kF32) {
-    float *dst = static_cast<float *>(o) + base + lane * DL;
-#pragma unroll
-    for (int j = 0; j < DL; ++j) dst[j] = acc[j];
+    *reinterpret_cast<float4 *>(static_cast<float *>(o) + base + 4 * lane) = acc;
   } else {
-    uint16_t *dst = static_cast<uint16_t *>(o) + base + lane * DL;
-#pragma unroll
-    for (int j = 0; j < DL; ++j) dst[j] = f32_to_bf16_rne(acc[j]);
+    const uint32_t lo = f32_to_bf16_rne(acc.x) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.y)) << 16);
+    const uint32_t hi = f32_to_bf16_rne(acc.z) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.w)) << 16);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(o) + base + 4 * lane) = make_uint2(lo, hi);
   }
 }
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void merge_verify_kernel(Plan P) {
   const int lane = threadIdx.x % kWave;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + threadIdx.x / kWave;
@@ -107,9 +163,9 @@ __global__ __launch_bounds__(256) void merge_verify_kernel(Plan P) {
   const int r = i * P.G + (h % P.G);
   const int64_t prow = (static_cast<int64_t>(b) * P.Hkv + g) * P.R + r;
   const int64_t stride = static_cast<int64_t>(P.B) * P.Hkv * P.R;
-  float acc[D / 64];
+  float4 acc;
   float lse;
-  merge_row<D>(P.o_part, P.lse_part, P.n_parts, stride, prow, lane, acc, &lse);
+  merge_row<D, F16>(P.o_part, P.lse_part, P.o_scale, P.n_parts, stride, prow, lane, &acc, &lse);
   store_row<D>(P.o, P.out_dtype, row * D, acc, lane);
   if (lane == 0) P.lse[row] = lse;
 }
@@ -122,9 +178,9 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const float *o_parts,
   const int lane = threadIdx.x % kWave;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + threadIdx.x / kWave;
   if (row >= n_rows) return;
-  float acc[D / 64];
+  float4 acc;
   float l;
-  merge_row<D>(o_parts, lse_parts, n_parts, n_rows, row, lane, acc, &l);
+  merge_row<D, false>(o_parts, lse_parts, nullptr, n_parts, n_rows, row, lane, &acc, &l);
   store_row<D>(o, out_dtype, row * D, acc, lane);
   if (lane == 0) lse[row] = l;
 }
@@ -193,10 +249,17 @@ hipError_t launch_tree_mask(const int32_t *parent, uint64_t *anc, int batch, int
 hipError_t launch_merge_verify(const Plan &p, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(p.B) * p.N * p.Hq;
   dim3 grid(static_cast<unsigned>((rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock));
-  if (p.D == 64)
-    hipLaunchKernelGGL(merge_verify_kernel<64>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(merge_verify_kernel<128>, grid, dim3(256), 0, s, p);
+  if (p.D == 64) {
+    if (p.part_f16)
+      hipLaunchKernelGGL((merge_verify_kernel<64, true>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((merge_verify_kernel<64, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (p.part_f16)
+      hipLaunchKernelGGL((merge_verify_kernel<128, true>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((merge_verify_kernel<128, false>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

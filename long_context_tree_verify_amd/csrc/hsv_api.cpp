@@ -52,6 +52,18 @@ hsv_status check_desc(const hsv_verify_desc *d, bool sparse) {
   return HSV_OK;
 }
 
+// Workspace of a plan: the partial rows (fp32, or fp16 plus a per-row scale),
+// their LSEs, and the validation error word; each region 256-byte aligned.
+size_t workspace_bytes(const Plan &p) {
+  const size_t rows = static_cast<size_t>(p.n_parts) * p.B * p.Hkv * p.R;
+  size_t off = 0;
+  off += align_up(rows * p.D * (p.part_f16 ? 2 : sizeof(float)));  // o_part
+  off += align_up(rows * sizeof(float));                           // lse_part
+  if (p.part_f16) off += align_up(rows * sizeof(float));            // o_scale
+  off += kAlign;                                                   // error word
+  return off;
+}
+
 // Resolve the descriptor into a launch plan (no pointers yet) and the bytes
 // of workspace it needs.
 hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_bytes) {
@@ -124,12 +136,8 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
     p->tree_slot = -1;
     p->n_slots = p->n_splits;
     p->n_parts = p->n_slots * p->kgroups;
-    const size_t rows = static_cast<size_t>(p->n_parts) * p->B * p->Hkv * p->R;
-    size_t off = 0;
-    off += align_up(rows * p->D * sizeof(float));  // o_part
-    off += align_up(rows * sizeof(float));         // lse_part
-    off += kAlign;                                 // error word
-    *ws_bytes = off;
+    p->part_f16 = 1;
+    *ws_bytes = workspace_bytes(*p);
     return HSV_OK;
   }
 
@@ -161,13 +169,8 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
   p->tree_slot = with_tree ? p->n_splits : -1;
   p->n_slots = p->n_splits + (with_tree ? 1 : 0);
   p->n_parts = p->n_slots * p->kgroups;
-
-  const size_t rows = static_cast<size_t>(p->n_parts) * p->B * p->Hkv * p->R;
-  size_t off = 0;
-  off += align_up(rows * p->D * sizeof(float));  // o_part
-  off += align_up(rows * sizeof(float));         // lse_part
-  off += kAlign;                                 // error word
-  *ws_bytes = off;
+  p->part_f16 = 0;
+  *ws_bytes = workspace_bytes(*p);
   return HSV_OK;
 }
 
@@ -175,9 +178,14 @@ void carve_workspace(Plan *p, void *ws) {
   char *base = static_cast<char *>(ws);
   const size_t rows = static_cast<size_t>(p->n_parts) * p->B * p->Hkv * p->R;
   p->o_part = reinterpret_cast<float *>(base);
-  base += align_up(rows * p->D * sizeof(float));
+  base += align_up(rows * p->D * (p->part_f16 ? 2 : sizeof(float)));
   p->lse_part = reinterpret_cast<float *>(base);
   base += align_up(rows * sizeof(float));
+  p->o_scale = nullptr;
+  if (p->part_f16) {
+    p->o_scale = reinterpret_cast<float *>(base);
+    base += align_up(rows * sizeof(float));
+  }
   p->err = reinterpret_cast<int32_t *>(base);
 }
 

@@ -39,9 +39,12 @@ struct Plan {
   // outputs
   void *o;
   float *lse;
-  // workspace partials: o_part [n_parts][B][Hkv][R][D], lse_part [n_parts][B][Hkv][R]
+  // workspace partials: o_part [n_parts][B][Hkv][R][D], lse_part [n_parts][B][Hkv][R].
+  // With part_f16, o_part holds fp16 rows and o_scale [n_parts][B][Hkv][R] the
+  // power of two each row was divided by (row = o_scale * fp16 row).
   float *o_part;
   float *lse_part;
+  float *o_scale;
   int32_t *err;             // validation error word (workspace)
 
   int32_t B, N, Hq, Hkv, G, D, R, cap;
@@ -54,6 +57,7 @@ struct Plan {
   int32_t has_prefix;       // the prefix part is included
   int32_t has_tree;         // the draft (tree) part is included
   int32_t unified;          // slot layout (see above)
+  int32_t part_f16;         // partial rows stored as scaled fp16
   int32_t tree_slot;        // slot index of the tree part (separate layout), or -1
   int32_t n_slots;          // n_splits + (tree_slot >= 0)
   int32_t kgroups;          // partial results per slot workgroup

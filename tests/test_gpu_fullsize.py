@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from util import assert_parity, device_inputs, log, run_hip
+from util import assert_parity, device_inputs, errors, log, run_hip
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,8 @@ def test_full_size_sampled_rows(hsv, gpu, name):
                                       kv_idx=inp.kv_idx, bf16=inp.is_bf16, rows=rows)
     got_o = np.stack([o_np[b, i, h] for b, i, h in rows])
     got_l = np.array([l_np[b, i, h] for b, i, h in rows])
+    o_err, l_err = errors(got_o, got_l, o_ref, l_ref)
+    log(f"full-size {name}: max|dO| = {o_err:.3e}, max rel dLSE = {l_err:.3e}")
     assert_parity(got_o, got_l, o_ref, l_ref, name)
     del dev
     torch.cuda.empty_cache()
