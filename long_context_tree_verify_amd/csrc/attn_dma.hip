@@ -250,12 +250,14 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   float m_run = kNegInf, l_run = 0.f;
   const float cs = P.scale_log2;
 
-  // S^T = K . Q^T for one 32-key block (block kb of the tile in stage st).
-  auto qk_block = [&](lds_char *const st, const int kb, floatx16 &sv) {
-    bf16x8 ka[8];
+  // K operands of one 32-key block (block kb of the tile in stage st), and
+  // S^T = K . Q^T from them.
+  auto read_k = [&](lds_char *const st, const int kb, bf16x8 (&ka)[8]) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       ka[ks] = *(const lds_bf16x8 *)(st + k_base + kb * 8192 + (ks >> 1) * 1024 + (ks & 1) * 512);
+  };
+  auto qk_mfma = [&](const bf16x8 (&ka)[8], floatx16 &sv) {
     sv = floatx16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -380,7 +382,11 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   wait_tile_and_sync(min(n_tiles - 1, kAhead - 1));
   if (kAhead < n_tiles) issue_tile(kAhead);
   floatx16 s_cur;
-  qk_block(lds, 0, s_cur);
+  {
+    bf16x8 ka[8];
+    read_k(lds, 0, ka);
+    qk_mfma(ka, s_cur);
+  }
   for (int t = 0; t < n_blocks; ++t) {
     const int j = t >> 1, kb = t & 1;
     lds_char *const st = lds + (j % kStages) * kStageBytes;
@@ -389,12 +395,16 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
       wait_tile_and_sync(min(n_tiles - 2 - j, kAhead - 1));
       if (j + 1 + kAhead < n_tiles) issue_tile(j + 1 + kAhead);
     }
-    if (t0 + 32 > mask_from) apply_mask(s_cur, t0);
+    // the next block's K operands first (its MFMAs wait on them), then this
+    // block's V operands (needed only after the softmax)
+    bf16x8 ka[8];
+    read_k(lds + (((t + 1) >> 1) % kStages) * kStageBytes, (t + 1) & 1, ka);
     bf16x8 va[4][2];
     read_v(st, kb, va);
+    if (t0 + 32 > mask_from) apply_mask(s_cur, t0);
     floatx16 s_nxt;
     bf16x8 pb[2];
-    qk_block(lds + (((t + 1) >> 1) % kStages) * kStageBytes, (t + 1) & 1, s_nxt);
+    qk_mfma(ka, s_nxt);
     float sum = fast_p(s_cur, pb);
     // Keep the conversion ahead of the branch: otherwise the compiler sinks
     // it into the fast path, the fp32 probabilities stay live across the
