@@ -90,14 +90,20 @@ struct KeySource {
 
 // Cache row of key t, or -1 when the key does not exist (past the slot's end
 // or an out-of-range index).  Never reads outside idx[0, t_end).
-template <bool SPARSE>
-__device__ __forceinline__ int key_row(const KeySource &src, int t) {
+__device__ __forceinline__ int index_row(const KeySource &src, int t) {
   if (t >= src.t_end) return -1;
-  if (SPARSE && src.idx) {
-    const int p = src.idx[t];
-    return (p >= 0 && p < src.c) ? p : -1;
-  }
-  return src.off + t;
+  const int p = src.idx[t];
+  return (p >= 0 && p < src.c) ? p : -1;
+}
+
+// Cache row of key t0 + k.  A sparse slot's rows come from the tile's row
+// table in LDS (filled from the index list two tiles ahead, so the data loads
+// never wait on an index load); a dense slot's rows are contiguous.
+template <bool SPARSE>
+__device__ __forceinline__ int key_row(const KeySource &src, const int32_t *rows, int t0, int k) {
+  if (SPARSE && src.idx) return rows[k];
+  const int t = t0 + k;
+  return t < src.t_end ? src.off + t : -1;
 }
 
 // Branch-free 16-byte load: invalid rows read row 0 of this (b, kv head) and
@@ -109,8 +115,9 @@ __device__ __forceinline__ uint4 load_row_chunk(const uint4 *base, int row, int 
 
 template <class C, bool SPARSE>
 __device__ __forceinline__ void load_tile(Tile<C> &tl, const uint4 *kc, const uint4 *vc,
-                                          const KeySource &src, int t0, int tid) {
-  if (!SPARSE && t0 + C::TK <= src.t_end) {
+                                          const KeySource &src, const int32_t *rows, int t0,
+                                          int tid) {
+  if (!(SPARSE && src.idx) && t0 + C::TK <= src.t_end) {
     // a whole tile of contiguous rows: no per-key checks
     const int row0 = src.off + t0;
 #pragma unroll
@@ -135,7 +142,7 @@ __device__ __forceinline__ void load_tile(Tile<C> &tl, const uint4 *kc, const ui
   for (int i = 0; i < C::NKL; ++i) {
     const int item = tid + C::NT * i;
     const int key = item / C::CH, ch = item % C::CH;
-    const int row = item < C::TK * C::CH ? key_row<SPARSE>(src, t0 + key) : -1;
+    const int row = item < C::TK * C::CH ? key_row<SPARSE>(src, rows, t0, key) : -1;
     tl.k[i] = load_row_chunk(kc, row, ch, C::CH);
   }
 #pragma unroll
@@ -147,7 +154,7 @@ __device__ __forceinline__ void load_tile(Tile<C> &tl, const uint4 *kc, const ui
     const bool ok = item < C::TK / 4 * C::CH;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = ok ? key_row<SPARSE>(src, t0 + 4 * grp + r) : -1;
+      const int row = ok ? key_row<SPARSE>(src, rows, t0, 4 * grp + r) : -1;
       tl.v[i][r] = load_row_chunk(vc, row, ch, C::CH);
     }
   }
@@ -192,6 +199,8 @@ __device__ __forceinline__ void store_tile(const Tile<C> &tl, char *ks, char *vt
 template <class C, bool SPARSE>
 __global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
   __shared__ __attribute__((aligned(16))) char smem[2][C::BUF_BYTES];
+  // sparse slots: cache rows of tiles j, j+1, j+2 (ring of three)
+  __shared__ int32_t srows[SPARSE ? 3 : 1][SPARSE ? C::TK : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -292,8 +301,23 @@ __global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
   const float cs = P.scale_log2;
   const int kbase = kg * 32 * C::KBW;
 
+  // Row table of a sparse slot's tile (one thread per key).
+  const bool gather = SPARSE && src.idx != nullptr;
+  auto fill_rows = [&](int jt) -> int {
+    return tid < C::TK ? index_row(src, t_begin + jt * C::TK + tid) : -1;
+  };
+  if (gather) {
+    const int r0 = fill_rows(0), r1 = fill_rows(1);
+    if (tid < C::TK) {
+      srows[0][tid] = r0;
+      srows[1 % (SPARSE ? 3 : 1)][tid] = r1;
+    }
+    __syncthreads();
+  }
+  const int32_t *rows0 = &srows[0][0];
+
   Tile<C> tl;
-  load_tile<C, SPARSE>(tl, kc, vc, src, t_begin, tid);
+  load_tile<C, SPARSE>(tl, kc, vc, src, rows0, t_begin, tid);
   store_tile<C>(tl, smem[0], smem[0] + C::K_BYTES, tid);
   __syncthreads();
 
@@ -301,7 +325,11 @@ __global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
     const int buf = j & 1;
     const int t0 = t_begin + j * C::TK;
     const bool more = j + 1 < n_tiles;
-    if (more) load_tile<C, SPARSE>(tl, kc, vc, src, t0 + C::TK, tid);
+    if (more)
+      load_tile<C, SPARSE>(tl, kc, vc, src, &srows[SPARSE ? (j + 1) % 3 : 0][0], t0 + C::TK,
+                           tid);
+    // indices of tile j+2, written to the ring after this tile's compute
+    const int next_rows = gather && j + 2 < n_tiles ? fill_rows(j + 2) : -1;
 
     const char *ks = smem[buf];
     const char *vt = smem[buf] + C::K_BYTES;
@@ -407,6 +435,7 @@ __global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
     }
 
     if (more) store_tile<C>(tl, smem[buf ^ 1], smem[buf ^ 1] + C::K_BYTES, tid);
+    if (gather && j + 2 < n_tiles && tid < C::TK) srows[SPARSE ? (j + 2) % 3 : 0][tid] = next_rows;
     __syncthreads();
   }
 
