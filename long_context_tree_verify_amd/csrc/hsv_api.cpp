@@ -148,7 +148,7 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
       target = d->num_splits;
     } else if (p->kernel == kKernValu) {
       const int64_t units = static_cast<int64_t>(p->B) * p->Hkv;
-      target = std::min<int64_t>(ceil_div(2 * kPlanCUs, units), ceil_div(keys, 4 * tile));
+      target = std::min<int64_t>(ceil_div(2 * kPlanCUs, units), ceil_div(keys, tile));
     } else {
       // One workgroup per CU (each holds the CU's LDS); split the prefix so
       // the (split, b, kv head, row chunk) workgroups cover the CUs, and

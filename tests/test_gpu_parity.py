@@ -88,6 +88,29 @@ def test_dense_parity_small(hsv, gpu, name, over):
     assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, name)
 
 
+# The 256-row kernel walks prefix and draft rows as one key range: contexts
+# around its 32-key block and 64-key tile boundaries put the draft rows
+# across blocks; c = 0 leaves only the draft block; ragged batches give
+# sequences whose later splits are empty.
+DMA_EDGE_CASES = [
+    (("ctx", (c, c)), ("batch", 1)) for c in (0, 1, 31, 32, 33, 63, 64, 65, 100, 1056)
+] + [
+    (("ctx", (0, 200)), ("batch", 3)),
+    (("ctx", (60, 2000)), ("batch", 3), ("n_draft", 50)),
+]
+
+
+@pytest.mark.parametrize("over", DMA_EDGE_CASES)
+def test_dma_path_edges(hsv, gpu, over):
+    inp = cached_inputs("tree32k", over)
+    log(f"dma edge {dict(over)} ctx={inp.ctx_lens.tolist()}")
+    dev = device_inputs(inp, gpu)
+    o_ref, l_ref = _oracle_all(inp)
+    for splits in (0, 3, 64):
+        o, lse = run_hip(hsv, inp, dev, num_splits=splits)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"splits={splits}")
+
+
 def test_tiny_fp32_is_tight(hsv, gpu):
     inp = cached_inputs("tiny_tree")
     dev = device_inputs(inp, gpu)
