@@ -88,9 +88,9 @@ typedef enum hsv_dtype { HSV_F32 = 0, HSV_BF16 = 1 } hsv_dtype;
  * Each alone is one of the two partial attentions of LongSpec section 2.C. */
 #define HSV_FLAG_NO_PREFIX 2u
 #define HSV_FLAG_NO_TREE 4u
-/* Run one phase only.  A verify call is two phases: PARTIALS (the prefix
- * splits and the tree part, written to the workspace) and MERGE (the exact
- * log-sum-exp combination into o and lse).  A MERGE-only call must follow a
+/* Run one phase only.  A verify call is two phases: PARTIALS (partial
+ * attentions over splits of the key set, written to the workspace) and MERGE
+ * (the exact log-sum-exp combination into o and lse).  A MERGE-only call must follow a
  * PARTIALS-only call with the same descriptor and workspace on the same
  * stream (or be otherwise ordered after it).  Neither or both bits: both
  * phases.  Lets a caller time the phases apart or place work between them. */
@@ -111,7 +111,12 @@ typedef struct hsv_verify_desc {
   int32_t in_dtype;    /* hsv_dtype of q, k, v                                  */
   int32_t out_dtype;   /* hsv_dtype of o                                        */
   float scale;         /* score scale; 0 means 1/sqrt(head_dim)                 */
-  int32_t num_splits;  /* split count over the prefix; 0 = automatic, else 1..256 */
+  int32_t num_splits;  /* key splits; 0 = automatic, else 1..256.  Dense bf16  */
+                       /* calls with D = 128 and more than 128 grouped rows    */
+                       /* (G*N) split prefix and draft rows as one range;      */
+                       /* other calls split the prefix (or index set) and add  */
+                       /* one part for the draft tree.  Results do not depend  */
+                       /* on the split count beyond rounding.                  */
   uint32_t flags;      /* HSV_FLAG_* bits                                       */
 } hsv_verify_desc;
 
