@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libhsv.so")
 BUILD = os.path.join(ROOT, "_build", "hsv")
 ARCH = "gfx950"
 
-SOURCES = ["hsv_api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_dma.hip", "aux_kernels.hip"]
+SOURCES = ["hsv_api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_dma.hip", "attn_dma_small.hip", "aux_kernels.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -28,6 +28,14 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+
+# Per-source additions.  The small-group kernel runs one wave per SIMD, and
+# with the AGPRs free the compiler would keep its MFMA accumulators there and
+# copy them back for every softmax; the VGPR form avoids the copies.
+EXTRA = {
+    "attn_dma_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
 
 
 def hipcc() -> str:
@@ -39,7 +47,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

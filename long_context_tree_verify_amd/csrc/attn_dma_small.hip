@@ -1,0 +1,405 @@
+// Partial verification attention for small query groups on gfx950: at most
+// 32 grouped rows per KV head (e.g. 4 query heads x an 8-token draft block),
+// bf16, D = 128, dense prefix plus draft rows as one key range.
+//
+// With 32 query rows every K/V byte feeds only 32 x 128 x 2 multiply-adds,
+// so the kernel is an HBM stream and its job is to keep enough bytes in
+// flight.  One workgroup owns one (split, sequence, KV head); its four waves
+// take every fourth 32-key block of the split, each with its own online
+// softmax, and merge their four results through LDS at the end.  Each wave
+// moves its blocks HBM -> LDS with global_load_lds_dwordx4 into a private
+// two-stage ring and waits only on its own DMA (s_waitcnt vmcnt), so the loop
+// has no workgroup barrier and the four streams drift freely.
+//
+// Inside a block everything is as in the 256-row kernel (attn_dma.hip): the
+// 1 KB DMA blocks (K: (chunk%4)*256 + (key%16)*16, V: (key%16)*64 +
+// (chunk%4)*16), S^T = K.Q^T and O^T += V^T.P^T on v_mfma_f32_32x32x16_bf16
+// with one lane per query column, V^T by ds_read_b64_tr_b16, the log2-domain
+// softmax with a fast path and exact fp32 row sums, and the unified key range
+// [0, c+N) whose rows at or past c are masked by the ancestor bits.  The
+// split's result is written as a scaled-fp16 partial row (see attn_dma.hip).
+#include "common.hpp"
+#include "launch.h"
+
+namespace hsv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+constexpr int kWaves = 4;                     // waves per workgroup, each on its own blocks
+constexpr int kNT = kWaves * 64;
+constexpr int kRows = 32;                     // grouped query rows (one MFMA column block)
+constexpr int kBK = 32;                       // keys per block
+constexpr int kD = 128;
+constexpr int kRowBytes = kD * 2;
+constexpr int kHalfBytes = kBK * kRowBytes;   // K (or V) of one block: 8 KB
+constexpr int kBlockBytes = 2 * kHalfBytes;   // 16 KB
+constexpr int kRing = 2;                      // stages per wave
+constexpr int kWaveLds = kRing * kBlockBytes; // 32 KB
+constexpr int kDmaPerBlock = 2 * kHalfBytes / 1024;  // 16 one-KB DMA instructions
+// Epilogue: each wave's 32 x 128 fp32 accumulator rows (padded) and row stats.
+constexpr int kEpiRow = kD * 4 + 16;
+constexpr int kEpiBytes = kWaves * kRows * kEpiRow + 2 * kWaves * kRows * 4;
+constexpr int kSmemBytes = kWaves * kWaveLds > kEpiBytes ? kWaves * kWaveLds : kEpiBytes;
+
+constexpr float kSumLimit = 65536.f;  // as in attn_dma.hip
+
+// (M0 is clobbered on purpose: nothing else in these kernels uses it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait for this wave's DMA of the current block; the next block's 16 DMA
+// instructions may stay in flight.
+__device__ __forceinline__ void wait_block(bool next_in_flight) {
+  static_assert(kDmaPerBlock == 16, "the immediate below");
+  if (next_in_flight)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int BH = P.B * P.Hkv;
+  const int bg = blockIdx.x % BH;
+  const int slot = blockIdx.x / BH;
+  const int b = bg / P.Hkv, g = bg % P.Hkv;
+
+  // ---- key range of this slot (prefix then draft rows) ----------------------
+  const int c = min(max(P.ctx_lens[b], 0), P.cap - P.N);
+  const int lo = P.has_prefix ? 0 : c;
+  const int hi = P.has_tree ? c + P.N : c;
+  const int t_begin = lo + slot * P.keys_per_split;
+  const int t_end = min(t_begin + P.keys_per_split, hi);
+  const int n_blocks = t_end > t_begin ? (t_end - t_begin + kBK - 1) / kBK : 0;
+  const int row_last = t_end - 1;
+  const bool tree = t_end > c;
+  const int mask_from = min(c, t_end);
+
+  const int r = l32;  // this lane's grouped row
+  const int64_t prow = (static_cast<int64_t>(slot) * BH + bg) * P.R + r;
+
+  if (n_blocks == 0) {
+    if (wave == 0 && hf == 0 && r < P.R) {
+      P.lse_part[prow] = kNegInf;
+      P.o_scale[prow] = 1.f;
+    }
+    return;
+  }
+
+  // this wave's blocks: i = wave, wave + 4, ...
+  const int my_n = wave < n_blocks ? (n_blocks - wave + kWaves - 1) / kWaves : 0;
+
+  const int64_t kv_row0 = static_cast<int64_t>(bg) * P.cap;
+  const char *kbytes = static_cast<const char *>(P.k) + kv_row0 * kRowBytes;
+  const char *vbytes = static_cast<const char *>(P.v) + kv_row0 * kRowBytes;
+  lds_char *const lds = (lds_char *)(smem);
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave * kWaveLds;
+
+  // DMA lane offsets inside a block (K block kb: key (kb/4)*16 + lane%16,
+  // chunk (kb%4)*4 + lane/16; V block vb: key (vb/4)*16 + lane/4, chunk
+  // (vb%4)*4 + lane%4).
+  auto k_key = [&](int kb) { return (kb >> 2) * 16 + (lane & 15); };
+  auto k_chunk = [&](int kb) { return ((kb & 3) * 4 + (lane >> 4)) * 16; };
+  auto v_key = [&](int vb) { return (vb >> 2) * 16 + (lane >> 2); };
+  auto v_chunk = [&](int vb) { return ((vb & 3) * 4 + (lane & 3)) * 16; };
+
+  // this wave's DMA of its k-th block into ring stage k % 2
+  auto issue_block = [&](const int k) {
+    const int row_first = t_begin + (wave + kWaves * k) * kBK;
+    const int lim = row_last - row_first;  // last valid key of the block
+    const char *kt = kbytes + static_cast<int64_t>(row_first) * kRowBytes;
+    const char *vt = vbytes + static_cast<int64_t>(row_first) * kRowBytes;
+    const uint32_t st = ring0 + (k & 1) * kBlockBytes;
+    if (lim >= kBK - 1) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        dma16(kt, k_key(x) * kRowBytes + k_chunk(x), st + x * 1024);
+        dma16(vt, v_key(x) * kRowBytes + v_chunk(x), st + kHalfBytes + x * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        dma16(kt, min(k_key(x), lim) * kRowBytes + k_chunk(x), st + x * 1024);
+        dma16(vt, min(v_key(x), lim) * kRowBytes + v_chunk(x), st + kHalfBytes + x * 1024);
+      }
+    }
+  };
+
+  // prologue: this wave's first two blocks, before the query loads
+  if (my_n > 0) issue_block(0);
+  if (my_n > 1) issue_block(1);
+
+  // ---- this lane's query (B operand of S^T = K.Q^T), tree mask word --------
+  const uint4 *qv = static_cast<const uint4 *>(P.q);
+  bf16x8 qf[8];
+  uint64_t anc_q = 0;
+  {
+    const bool ok = r < P.R;
+    const int i = ok ? r / P.G : 0;
+    const int h = g * P.G + (ok ? r % P.G : 0);
+    const int64_t qrow = (static_cast<int64_t>(b) * P.N + i) * P.Hq + h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 u = ok ? qv[qrow * (kD / 8) + 2 * ks + hf] : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+    if (tree) {
+      if (P.anc) {
+        anc_q = P.anc[static_cast<int64_t>(b) * P.N + i];
+      } else {
+        bool bad;
+        const uint64_t a = tree_ancestors(P.parent + static_cast<int64_t>(b) * P.N, P.N, lane,
+                                          &bad);
+        anc_q = shfl_u64(a, i);
+      }
+    }
+  }
+  // Consume the query loads now; the compiler does not count the DMA, so its
+  // wait is vmcnt(0) and the prologue blocks have landed too.
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
+  asm volatile("" ::"v"(anc_q));
+
+  const int k_base = (l32 >> 4) * 4096 + hf * 256 + (l32 & 15) * 16;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int v_base = kHalfBytes + (4 * hf + (s16 >> 2)) * 64 +
+                     (2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+
+  floatx16 o_acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o_acc[db] = floatx16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const float cs = P.scale_log2;
+
+  for (int k = 0; k < my_n; ++k) {
+    wait_block(k + 1 < my_n);
+    lds_char *const st = lds + wave * kWaveLds + (k & 1) * kBlockBytes;
+    const int t0 = t_begin + (wave + kWaves * k) * kBK;
+
+    // S^T = K . Q^T
+    bf16x8 ka[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      ka[ks] = *(const lds_bf16x8 *)(st + k_base + (ks >> 1) * 1024 + (ks & 1) * 512);
+    // V^T operands, needed after the softmax
+    bf16x4 t4[4][2][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        lds_char *vp = st + v_base + half * 4096 + db * 1024;
+        t4[db][half][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp));
+        t4[db][half][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp + 512));
+      }
+    floatx16 sv = floatx16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sv, 0, 0, 0);
+
+    // mask: keys past the slot's end, draft rows by ancestor bits (lane
+    // value e is key t0 + 4*hf + 8*(e/4) + e%4)
+    if (t0 + kBK > mask_from) {
+      const int base = t0 + 4 * hf;
+      const int room = t_end - base;
+      const int pre = c - base;
+      uint32_t keep = pre <= 0 ? 0u : pre >= 32 ? ~0u : ((1u << pre) - 1u);
+      if (tree) {
+        const int sh = -pre;
+        keep |= sh >= 64 || sh <= -32 ? 0u
+                : sh >= 0         ? static_cast<uint32_t>(anc_q >> sh)
+                                  : static_cast<uint32_t>(anc_q << (-sh));
+      }
+      keep &= room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int bit = 8 * (e >> 2) + (e & 3);
+        sv[e] = ((keep >> bit) & 1u) ? sv[e] : kNegInf;
+      }
+    }
+
+    // softmax against the running reference (fast path), exact fp32 sum
+    float p[16];
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(fmaf(sv[e], cs, -m_run));
+      sum += p[e];
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      floatx8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = p[8 * half + e];
+      pb[half] = __builtin_convertvector(x, bf16x8);
+    }
+    // keep the conversion ahead of the branch (see attn_dma.hip)
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
+    if (__builtin_expect(__any(!(sum <= kSumLimit) || m_run == kNegInf), 0)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * cs;
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = fast_exp2(fmaf(sv[e], cs, -m_use));
+        sum += p[e];
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        floatx8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[8 * half + e];
+        pb[half] = __builtin_convertvector(x, bf16x8);
+      }
+      if (__any(m_run != kNegInf && alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
+      }
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    l_run += sum;
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 a = __builtin_shufflevector(t4[db][half][0], t4[db][half][1], 0, 1, 2, 3, 4,
+                                                 5, 6, 7);
+        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[half], o_acc[db], 0, 0, 0);
+      }
+
+    // refill this stage with block k+2 once its operands have been read
+    if (k + 2 < my_n) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_block(k + 2);
+    }
+  }
+
+  // ---- merge the four waves' results through LDS ---------------------------
+  // Each wave's row statistics (log2-domain reference and sum) and its
+  // unnormalised accumulator rows; then every thread combines 16 values of
+  // one row: weights 2^(m_w - M) / L with L = sum_w l_w 2^(m_w - M).
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  __syncthreads();  // every wave is done with its ring
+  float *stat_m = reinterpret_cast<float *>(smem + kWaves * kRows * kEpiRow);
+  float *stat_l = stat_m + kWaves * kRows;
+  if (hf == 0) {
+    stat_m[wave * kRows + l32] = l_tot > 0.f ? m_run : kNegInf;
+    stat_l[wave * kRows + l32] = l_tot;
+  }
+  char *ep = smem + wave * kRows * kEpiRow;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float4 v4;
+      v4.x = o_acc[db][4 * jj + 0];
+      v4.y = o_acc[db][4 * jj + 1];
+      v4.z = o_acc[db][4 * jj + 2];
+      v4.w = o_acc[db][4 * jj + 3];
+      *reinterpret_cast<float4 *>(ep + l32 * kEpiRow + (32 * db + 8 * jj + 4 * hf) * 4) = v4;
+    }
+  __syncthreads();
+
+  // thread -> (row, 16 features): 8 threads per row, rows 0..31
+  const int row = tid >> 3, f0 = (tid & 7) * 16;
+  float mw[kWaves], lw[kWaves];
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = stat_m[w * kRows + row];
+    lw[w] = stat_l[w * kRows + row];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f, sc[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    sc[w] = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - M);
+    L += lw[w] * sc[w];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float o16[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o16[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float wt = sc[w] * inv;
+    const float *src = reinterpret_cast<const float *>(smem + (w * kRows + row) * kEpiRow) + f0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o16[e] = fmaf(wt, src[e], o16[e]);
+  }
+  // scaled fp16: the row's largest |value| in [0.5, 1), scale to o_scale
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o16[e]));
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  int ex = 0;
+  if (amax > 0.f && amax < __builtin_huge_valf()) (void)frexpf(amax, &ex);
+  const float mul = ldexpf(1.f, -ex);
+  if (row < P.R) {
+    const int64_t orow = (static_cast<int64_t>(slot) * BH + bg) * P.R + row;
+    halfx8 h0, h1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h0[e] = static_cast<_Float16>(o16[e] * mul);
+      h1[e] = static_cast<_Float16>(o16[8 + e] * mul);
+    }
+    _Float16 *dst = reinterpret_cast<_Float16 *>(P.o_part) + orow * kD + f0;
+    *reinterpret_cast<halfx8 *>(dst) = h0;
+    *reinterpret_cast<halfx8 *>(dst + 8) = h1;
+    if ((tid & 7) == 0) {
+      P.lse_part[orow] = L > 0.f ? (M + fast_log2(L)) * kLn2 : kNegInf;
+      P.o_scale[orow] = ldexpf(1.f, ex);
+    }
+  }
+}
+
+}  // namespace
+
+bool dma_small_supports(const Plan &p) {
+  return p.in_dtype == kBF16 && p.D == kD && p.n_sel == 0 && p.R <= kRows;
+}
+
+int dma_small_tile_keys() { return kWaves * kBK; }
+
+hipError_t launch_attn_partials_dma_small(const Plan &p, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(p.n_slots) * p.B * p.Hkv;
+  hipLaunchKernelGGL(attn_partial_dma_small, dim3(static_cast<unsigned>(blocks)), dim3(kNT), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
+}  // namespace hsv

@@ -104,6 +104,11 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
       p->kgroups = 1;
       p->row_chunks = static_cast<int32_t>(ceil_div(p->R, dma_rows_per_wg()));
       tile = dma_tile_keys();
+    } else if (dma_small_supports(*p)) {
+      p->kernel = kKernDmaSmall;
+      p->kgroups = 1;
+      p->row_chunks = 1;
+      tile = dma_small_tile_keys();
     }
   } else {
     p->kernel = kKernValu;
@@ -113,7 +118,7 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
 
   p->has_prefix = with_prefix;
   p->has_tree = with_tree;
-  p->unified = p->kernel == kKernDma256;
+  p->unified = p->kernel == kKernDma256 || p->kernel == kKernDmaSmall;
   if (p->unified) {
     // One key range per (b, kv head): prefix then draft rows.  One workgroup
     // per CU: as many splits as fit in one round of the CUs (splits of a
@@ -244,6 +249,7 @@ hipError_t launch_attn_partials(const Plan &p, hipStream_t s) {
   switch (p.kernel) {
     case kKernValu: return launch_attn_partials_valu(p, s);
     case kKernDma256: return launch_attn_partials_dma(p, s);
+    case kKernDmaSmall: return launch_attn_partials_dma_small(p, s);
     default: return launch_attn_partials_mfma(p, s);
   }
 }

@@ -27,6 +27,10 @@ hipError_t launch_attn_partials_dma(const Plan &p, hipStream_t s);
 bool dma_supports(const Plan &p);
 int dma_rows_per_wg();
 int dma_tile_keys();
+hipError_t launch_attn_partials_dma_small(const Plan &p, hipStream_t s);
+// The per-wave DMA variant for small groups: dense bf16, head_dim 128, <= 32 rows.
+bool dma_small_supports(const Plan &p);
+int dma_small_tile_keys();
 
 // Prefix splits and the tree part -> o_part / lse_part.
 hipError_t launch_attn_partials(const Plan &p, hipStream_t s);

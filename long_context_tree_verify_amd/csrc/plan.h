@@ -14,7 +14,8 @@ enum : int {
   kKernMfma64 = 2, // bf16 MFMA, <= 64 grouped rows, 4 key-waves
   kKernMfma128 = 3,// bf16 MFMA, <= 128 grouped rows, 2 row-waves x 2 key-waves
   kKernMfma256 = 4,// bf16 MFMA, 256-row chunks, register-staged tiles
-  kKernDma256 = 5  // bf16 MFMA, 256-row chunks, HBM->LDS DMA pipeline (dense, D=128)
+  kKernDma256 = 5, // bf16 MFMA, 256-row chunks, HBM->LDS DMA pipeline (dense, D=128)
+  kKernDmaSmall = 6 // bf16 MFMA, <= 32 rows, per-wave HBM->LDS DMA streams (dense, D=128)
 };
 
 // One verify call, resolved on the host.  Grouped row r of KV head g is

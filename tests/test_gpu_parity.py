@@ -101,9 +101,10 @@ DMA_EDGE_CASES = [
 
 
 @pytest.mark.parametrize("over", DMA_EDGE_CASES)
-def test_dma_path_edges(hsv, gpu, over):
-    inp = cached_inputs("tree32k", over)
-    log(f"dma edge {dict(over)} ctx={inp.ctx_lens.tolist()}")
+@pytest.mark.parametrize("wl", ["tree32k", "chain_b16"])   # 256 and 32 grouped rows
+def test_dma_path_edges(hsv, gpu, over, wl):
+    inp = cached_inputs(wl, over)
+    log(f"dma edge {wl} {dict(over)} ctx={inp.ctx_lens.tolist()}")
     dev = device_inputs(inp, gpu)
     o_ref, l_ref = _oracle_all(inp)
     for splits in (0, 3, 64):
