@@ -1,6 +1,8 @@
 // Partial verification attention for small query groups on gfx950: at most
 // 32 grouped rows per KV head (e.g. 4 query heads x an 8-token draft block),
-// bf16, D = 128, dense prefix plus draft rows as one key range.
+// bf16, D = 128.  The key set is one range: the dense prefix [0, c) or the
+// gathered index set (Dustin page, verification over the selected subset of
+// a fully indexed cache), followed by the N draft rows.
 //
 // With 32 query rows every K/V byte feeds only 32 x 128 x 2 multiply-adds,
 // so the kernel is an HBM stream and its job is to keep enough bytes in
@@ -18,6 +20,14 @@
 // softmax with a fast path and exact fp32 row sums, and the unified key range
 // [0, c+N) whose rows at or past c are masked by the ancestor bits.  The
 // split's result is written as a scaled-fp16 partial row (see attn_dma.hip).
+//
+// Sparse sets: key t < n_sel is cache row kv_idx[t], key n_sel + j is draft
+// row c + j.  Every DMA lane supplies its own address, so gathering costs
+// nothing extra on the data path; the row numbers of a block are themselves
+// fetched by a 4-byte-per-lane DMA into a per-wave two-slot LDS ring two
+// blocks ahead, so no load the compiler tracks ever sits between the DMA
+// waits.  Indices outside [0, c) are masked (a per-block 32-bit validity
+// word taken by ballot when the block's rows are read).
 #include "common.hpp"
 #include "launch.h"
 
@@ -48,7 +58,11 @@ constexpr int kDmaPerBlock = 2 * kHalfBytes / 1024;  // 16 one-KB DMA instructio
 // Epilogue: each wave's 32 x 128 fp32 accumulator rows (padded) and row stats.
 constexpr int kEpiRow = kD * 4 + 16;
 constexpr int kEpiBytes = kWaves * kRows * kEpiRow + 2 * kWaves * kRows * 4;
-constexpr int kSmemBytes = kWaves * kWaveLds > kEpiBytes ? kWaves * kWaveLds : kEpiBytes;
+constexpr int kStreamBytes = kWaves * kWaveLds;
+constexpr int kIdxSlot = 64 * 4;               // one block's row indices (64 lanes)
+constexpr int kIdxBytes = kWaves * 2 * kIdxSlot;
+constexpr int kSmemBytes =
+    (kStreamBytes > kEpiBytes ? kStreamBytes : kEpiBytes) + kIdxBytes;
 
 constexpr float kSumLimit = 65536.f;  // as in attn_dma.hip
 
@@ -64,18 +78,32 @@ __device__ __forceinline__ void dma16(const char *sbase, uint32_t voff, uint32_t
       : "v"(voff), "s"(sbase), "s"(lds_base)
       : "memory", "m0");
 }
+
+// Row indices of one block (64 lanes x 4 bytes; lanes 32..63 repeat 0..31).
+__device__ __forceinline__ void dma4(const char *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-// Wait for this wave's DMA of the current block; the next block's 16 DMA
-// instructions may stay in flight.
-__device__ __forceinline__ void wait_block(bool next_in_flight) {
-  static_assert(kDmaPerBlock == 16, "the immediate below");
-  if (next_in_flight)
+// s_waitcnt vmcnt(n) for the counts this kernel uses: 0, 16 (one block's 16
+// DMA instructions still in flight) and 17 (a block and one index fetch).
+__device__ __forceinline__ void wait_vm(int n) {
+  static_assert(kDmaPerBlock == 16, "the immediates below");
+  if (n >= 17)
+    asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
+  else if (n >= 16)
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
 
@@ -89,16 +117,19 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   const int slot = blockIdx.x / BH;
   const int b = bg / P.Hkv, g = bg % P.Hkv;
 
-  // ---- key range of this slot (prefix then draft rows) ----------------------
+  // ---- key range of this slot (prefix or index set, then draft rows) --------
+  // Keys [0, cpos) are the prefix (dense: rows 0..c-1; sparse: rows
+  // kv_idx[0..n_sel-1]), keys cpos + j are draft row c + j.
   const int c = min(max(P.ctx_lens[b], 0), P.cap - P.N);
-  const int lo = P.has_prefix ? 0 : c;
-  const int hi = P.has_tree ? c + P.N : c;
+  const int cpos = SPARSE ? P.n_sel : c;
+  const int lo = P.has_prefix ? 0 : cpos;
+  const int hi = P.has_tree ? cpos + P.N : cpos;
   const int t_begin = lo + slot * P.keys_per_split;
   const int t_end = min(t_begin + P.keys_per_split, hi);
   const int n_blocks = t_end > t_begin ? (t_end - t_begin + kBK - 1) / kBK : 0;
   const int row_last = t_end - 1;
-  const bool tree = t_end > c;
-  const int mask_from = min(c, t_end);
+  const bool tree = t_end > cpos;
+  const int mask_from = min(cpos, t_end);
 
   const int r = l32;  // this lane's grouped row
   const int64_t prow = (static_cast<int64_t>(slot) * BH + bg) * P.R + r;
@@ -128,8 +159,61 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   auto v_key = [&](int vb) { return (vb >> 2) * 16 + (lane >> 2); };
   auto v_chunk = [&](int vb) { return ((vb & 3) * 4 + (lane & 3)) * 16; };
 
+  // sparse: this wave's index ring, and the row-index fetch of its k-th block
+  const int32_t *idx_row = SPARSE ? P.kv_idx + static_cast<int64_t>(bg) * P.n_sel : nullptr;
+  const uint32_t iring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) +
+                          (kSmemBytes - kIdxBytes) + wave * 2 * kIdxSlot;
+  auto issue_idx = [&](const int k) {
+    const int t0 = t_begin + (wave + kWaves * k) * kBK;
+    const int t = min(t0 + (lane & 31), P.n_sel - 1);  // past the set: any valid index
+    dma4(reinterpret_cast<const char *>(idx_row), static_cast<uint32_t>(t) * 4,
+         iring0 + (k & 1) * kIdxSlot);
+  };
+  uint32_t vbits[2] = {~0u, ~0u};  // per-block validity (sparse), by k % 2
+
   // this wave's DMA of its k-th block into ring stage k % 2
   auto issue_block = [&](const int k) {
+    if constexpr (SPARSE) {
+      // rows of this lane's two K keys and two V keys, from the index ring
+      const int t0 = t_begin + (wave + kWaves * k) * kBK;
+      const int32_t *slot_idx =
+          reinterpret_cast<const int32_t *>(smem + (kSmemBytes - kIdxBytes) +
+                                            (wave * 2 + (k & 1)) * kIdxSlot);
+      // Keys past the range's end and out-of-range indices are masked; they
+      // load the row of the block's last key, which is in the key set (so its
+      // values are finite: a masked key's probability is 0, and 0 * NaN would
+      // still poison P.V).
+      auto row_at = [&](int t) {  // cache row of key t < t_end, or -1
+        if (t >= cpos) return c + (t - cpos);
+        const int p = slot_idx[t - t0];
+        return (p >= 0 && p < c) ? p : -1;
+      };
+      const int r_last = row_at(min(t0 + kBK, t_end) - 1);
+      const int safe = r_last >= 0 ? r_last : 0;
+      auto row_of = [&](int key) {
+        const int t = t0 + key;
+        const int rr = t < t_end ? row_at(t) : -1;
+        return rr >= 0 ? rr : safe;
+      };
+      // validity of the block's 32 keys (lane j < 32 answers for key j)
+      {
+        const int t = t0 + (lane & 31);
+        const int p = slot_idx[lane & 31];
+        const bool ok = t < t_end && (t >= cpos || (p >= 0 && p < c));
+        vbits[k & 1] = static_cast<uint32_t>(__ballot(ok));
+      }
+      const int rk0 = row_of(lane & 15), rk1 = row_of(16 + (lane & 15));
+      const int rv0 = row_of(lane >> 2), rv1 = row_of(16 + (lane >> 2));
+      const uint32_t st = ring0 + (k & 1) * kBlockBytes;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        dma16(kbytes, static_cast<uint32_t>(x < 4 ? rk0 : rk1) * kRowBytes + k_chunk(x),
+              st + x * 1024);
+        dma16(vbytes, static_cast<uint32_t>(x < 4 ? rv0 : rv1) * kRowBytes + v_chunk(x),
+              st + kHalfBytes + x * 1024);
+      }
+      return;
+    }
     const int row_first = t_begin + (wave + kWaves * k) * kBK;
     const int lim = row_last - row_first;  // last valid key of the block
     const char *kt = kbytes + static_cast<int64_t>(row_first) * kRowBytes;
@@ -150,9 +234,20 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     }
   };
 
-  // prologue: this wave's first two blocks, before the query loads
-  if (my_n > 0) issue_block(0);
-  if (my_n > 1) issue_block(1);
+  // prologue: this wave's first two blocks, before the query loads.  Sparse:
+  // indices of blocks 0 and 1, then blocks 0 and 1 with the indices of block
+  // 2 between them, which is the order the loop keeps (see below).
+  if constexpr (SPARSE) {
+    if (my_n > 0) issue_idx(0);
+    if (my_n > 1) issue_idx(1);
+    wait_vm(0);
+    if (my_n > 0) issue_block(0);
+    if (my_n > 2) issue_idx(2);
+    if (my_n > 1) issue_block(1);
+  } else {
+    if (my_n > 0) issue_block(0);
+    if (my_n > 1) issue_block(1);
+  }
 
   // ---- this lane's query (B operand of S^T = K.Q^T), tree mask word --------
   const uint4 *qv = static_cast<const uint4 *>(P.q);
@@ -196,8 +291,12 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   float m_run = kNegInf, l_run = 0.f;
   const float cs = P.scale_log2;
 
+  // Order of this wave's DMA: ..., data(k), [idx(k+2), data(k+1)], [idx(k+3),
+  // data(k+2)], ...  so data(k) is complete once at most 16 * [k+1 < n] +
+  // [k+2 < n] instructions are outstanding, and idx(k+2) once data(k+1)'s 16
+  // are.
   for (int k = 0; k < my_n; ++k) {
-    wait_block(k + 1 < my_n);
+    wait_vm((k + 1 < my_n ? 16 : 0) + (SPARSE && k + 2 < my_n ? 1 : 0));
     lds_char *const st = lds + wave * kWaveLds + (k & 1) * kBlockBytes;
     const int t0 = t_begin + (wave + kWaves * k) * kBK;
 
@@ -221,12 +320,13 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     for (int ks = 0; ks < 8; ++ks)
       sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sv, 0, 0, 0);
 
-    // mask: keys past the slot's end, draft rows by ancestor bits (lane
-    // value e is key t0 + 4*hf + 8*(e/4) + e%4)
-    if (t0 + kBK > mask_from) {
+    // mask: keys past the slot's end, draft rows by ancestor bits, invalid
+    // indices (lane value e is key t0 + 4*hf + 8*(e/4) + e%4)
+    const uint32_t vb = SPARSE ? vbits[k & 1] : ~0u;
+    if (t0 + kBK > mask_from || vb != ~0u) {
       const int base = t0 + 4 * hf;
       const int room = t_end - base;
-      const int pre = c - base;
+      const int pre = cpos - base;
       uint32_t keep = pre <= 0 ? 0u : pre >= 32 ? ~0u : ((1u << pre) - 1u);
       if (tree) {
         const int sh = -pre;
@@ -235,6 +335,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
                                   : static_cast<uint32_t>(anc_q << (-sh));
       }
       keep &= room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
+      keep &= vb >> (4 * hf);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int bit = 8 * (e >> 2) + (e & 3);
@@ -301,8 +402,14 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
       }
 
     // refill this stage with block k+2 once its operands have been read
+    // (the index fetch of block k+3 reuses the slot of block k+1, whose rows
+    // were read before block k+1 was issued)
     if (k + 2 < my_n) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (SPARSE) {
+        wait_vm(16);  // idx(k+2) has landed
+        if (k + 3 < my_n) issue_idx(k + 3);
+      }
       issue_block(k + 2);
     }
   }
@@ -390,15 +497,21 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
 }  // namespace
 
 bool dma_small_supports(const Plan &p) {
-  return p.in_dtype == kBF16 && p.D == kD && p.n_sel == 0 && p.R <= kRows;
+  // sparse DMA offsets are 32-bit byte offsets from the (b, kv head) base
+  return p.in_dtype == kBF16 && p.D == kD && p.R <= kRows &&
+         (p.n_sel == 0 || static_cast<int64_t>(p.cap) * kRowBytes < (int64_t{1} << 32));
 }
 
 int dma_small_tile_keys() { return kWaves * kBK; }
 
 hipError_t launch_attn_partials_dma_small(const Plan &p, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(p.n_slots) * p.B * p.Hkv;
-  hipLaunchKernelGGL(attn_partial_dma_small, dim3(static_cast<unsigned>(blocks)), dim3(kNT), 0,
-                     s, p);
+  if (p.n_sel > 0)
+    hipLaunchKernelGGL(attn_partial_dma_small<true>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kNT), 0, s, p);
+  else
+    hipLaunchKernelGGL(attn_partial_dma_small<false>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kNT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -120,11 +120,12 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
   p->has_tree = with_tree;
   p->unified = p->kernel == kKernDma256 || p->kernel == kKernDmaSmall;
   if (p->unified) {
-    // One key range per (b, kv head): prefix then draft rows.  One workgroup
+    // One key range per (b, kv head): prefix (or index set) then draft rows.  One workgroup
     // per CU: as many splits as fit in one round of the CUs (splits of a
     // multiple of 32 keys), more only when the batch is ragged and a split
     // would exceed 64 tiles.
-    const int64_t keys = (with_prefix ? d->max_ctx : 0) + (with_tree ? d->n_draft : 0);
+    const int64_t keys = (with_prefix ? (sparse ? d->n_sel : d->max_ctx) : 0) +
+                         (with_tree ? d->n_draft : 0);
     const int64_t units = static_cast<int64_t>(p->B) * p->Hkv * p->row_chunks;
     int64_t target;
     if (d->num_splits > 0) {

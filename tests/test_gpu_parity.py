@@ -195,7 +195,26 @@ SPARSE_CASES = [
     (("ctx", (8000, 8000)), ("batch", 2), ("n_sel", 1000), ("n_recent", 200)),
     (("ctx", (3000, 3000)), ("batch", 3), ("n_sel", 77), ("n_recent", 10), ("n_draft", 5)),
     (("ctx", (600, 600)), ("batch", 1), ("n_sel", 600), ("n_recent", 96)),   # all selected
+    (("ctx", (500, 900)), ("batch", 2), ("n_sel", 1), ("n_sink", 0), ("n_recent", 1)),
+    (("ctx", (500, 900)), ("batch", 2), ("n_sel", 33), ("n_sink", 4), ("n_recent", 8)),
+    (("ctx", (300, 300)), ("batch", 1), ("n_sel", 100), ("n_recent", 20), ("n_draft", 3)),
 ]
+
+
+@pytest.mark.parametrize("over", SPARSE_CASES[3:])
+def test_sparse_splits_and_parts(hsv, gpu, over):
+    inp = cached_inputs("sparse64k", over, poison=True)
+    log(f"sparse splits/parts {dict(over)}")
+    dev = device_inputs(inp, gpu)
+    o_ref, l_ref = _oracle_all(inp)
+    for splits in (0, 2, 5):
+        o, lse = run_hip(hsv, inp, dev, num_splits=splits)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"splits={splits}")
+    for flag, part in ((hsv.HSV_FLAG_NO_TREE, oracle.PART_PREFIX),
+                       (hsv.HSV_FLAG_NO_PREFIX, oracle.PART_TREE)):
+        o, lse = run_hip(hsv, inp, dev, flags=flag)
+        o_p, l_p = _oracle_all(inp, parts=part)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_p, l_p, f"flags={flag}")
 
 
 @pytest.mark.parametrize("over", SPARSE_CASES)
