@@ -45,8 +45,7 @@ INFINITY_CACHE_BYTES = 256 * 2 ** 20
 # and the sources whose hash it records.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_partial_dma_tree32k_counters.md")
 KERNEL_SOURCES = ("long_context_tree_verify_amd/csrc/attn_dma.hip",
-                  "long_context_tree_verify_amd/csrc/common.hpp",
-                  "long_context_tree_verify_amd/csrc/plan.h")
+                  "long_context_tree_verify_amd/csrc/common.hpp")
 
 
 def log(msg):
@@ -272,10 +271,15 @@ def main(argv=None) -> int:
     nbytes = kv_bytes(inp)
     flops = step_flops(inp)
     traffic = recorded_traffic(wl.name) if kv_idx is None and bf else None
+    rows = wl.group * wl.n_draft
     if not bf:
         kernel_name = "attn_partial_valu"
-    elif kv_idx is None and wl.head_dim == 128 and wl.group * wl.n_draft > 128:
+    elif kv_idx is None and wl.head_dim == 128 and rows > 128:
         kernel_name = "attn_partial_dma (prefix + draft rows, split along keys)"
+    elif wl.head_dim == 128 and rows <= 32:
+        kernel_name = ("attn_partial_dma_small<sparse> (index set + draft rows, per-wave DMA)"
+                       if kv_idx is not None else
+                       "attn_partial_dma_small<dense> (prefix + draft rows, per-wave DMA)")
     else:
         kernel_name = "attn_partial_mfma (prefix or index-set splits, draft slot)"
     gbs = nbytes / (ms * 1e-3) / 1e9
