@@ -172,3 +172,62 @@ def gather_kv(k: np.ndarray, v: np.ndarray, kv_idx: np.ndarray):
     bi = np.arange(B)[:, None, None]
     gi = np.arange(Hkv)[None, :, None]
     return k[bi, gi, kv_idx], v[bi, gi, kv_idx]
+
+
+def _top_positions(scores: np.ndarray, pos: np.ndarray, k: int) -> np.ndarray:
+    """The k best positions: higher score first, NaN below every number,
+    -0 equal to +0, ties to the lower position."""
+    if k <= 0 or pos.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    s = np.asarray(scores, dtype=np.float64)
+    nan = np.isnan(s)
+    neg = np.where(nan, 0.0, -s)            # -0 and +0 compare equal
+    order = np.lexsort((pos, neg, nan))     # last key is the primary one
+    return pos[order[:k]]
+
+
+def select_kv_idx(draft_score: np.ndarray, target_score: np.ndarray, ctx_lens: np.ndarray,
+                  n_sel: int, n_sink: int, n_recent: int, n_draft_top: int) -> np.ndarray:
+    """Fixed-size verification index set per (sequence b, KV head g)
+    (Dustin page, methodology 1, hybrid attention aggregation; verification
+    workflow step 3: the compressed cache is formed from these positions).
+
+    Of the positions [0, c) with c = ctx_lens[b] (clipped to the score rows'
+    length): the first n_sink and the last n_recent are always kept; of the
+    positions between them, the n_draft_top best by the draft-lookahead score,
+    then the best by the target-historical score until n_sel positions are
+    chosen.  "Best" is `_top_positions`.  Output: int32 [B, Hkv, n_sel],
+    ascending; if fewer than n_sel positions exist the tail is -1.
+    Requires n_sink + n_recent <= n_sel.
+    """
+    draft_score = np.asarray(draft_score)
+    target_score = np.asarray(target_score)
+    B, Hkv, S = draft_score.shape
+    assert target_score.shape == (B, Hkv, S)
+    assert 0 <= n_sink and 0 <= n_recent and n_sink + n_recent <= n_sel and n_draft_top >= 0
+    out = np.full((B, Hkv, n_sel), -1, dtype=np.int32)
+    for b in range(B):
+        c = int(min(max(int(ctx_lens[b]), 0), S))
+        lo = min(n_sink, c)
+        hi = max(c - n_recent, lo)
+        protected = np.concatenate([np.arange(0, lo), np.arange(hi, c)]).astype(np.int64)
+        fill = n_sel - protected.size
+        cand = np.arange(lo, hi, dtype=np.int64)
+        for g in range(Hkv):
+            m = min(n_draft_top, fill, cand.size)
+            top_d = _top_positions(draft_score[b, g, cand], cand, m)
+            rest_pos = np.setdiff1d(cand, top_d, assume_unique=True)
+            rest = min(fill - m, rest_pos.size)
+            top_t = _top_positions(target_score[b, g, rest_pos], rest_pos, rest)
+            sel = np.sort(np.concatenate([protected, top_d, top_t]))
+            out[b, g, :sel.size] = sel
+    return out
+
+
+def recall_rate(lse_subset: np.ndarray, lse_full: np.ndarray) -> np.ndarray:
+    """Attention recall rate of a key subset for each query row: the share of
+    the full prefix's softmax mass that falls on the subset,
+    sum_{t in I} exp(s_t) / sum_{t < c} exp(s_t) = exp(lse_I - lse_full)
+    (the pages name the rate without defining it; this is the plain
+    reading)."""
+    return np.exp(np.asarray(lse_subset, dtype=np.float64) - np.asarray(lse_full, np.float64))
