@@ -141,6 +141,60 @@ def cpu_baseline(inp, target_s: float):
             "step_s": round(step_s, 4)}
 
 
+# Verification index-set selection on the sparse workload's shape: 8
+# sequences x 8 KV heads, 65536-position importance maps, a 4096-entry set
+# of 4 sinks, a 512-token window, 1790 by the draft map, the rest by the
+# target map.
+SELECT_SHAPE = dict(batch=8, n_kv_heads=8, score_len=65536, n_sel=4096, n_sink=4,
+                    n_recent=512, n_draft_top=1790, seed=505)
+
+
+def measure_selection(hsv, dev, steps: int, warmup: int):
+    """Average duration of one hsv_select_kv_idx launch (HIP events around a
+    graph of `steps` launches on the stream they run on) and the algorithmic
+    bytes it moves: each candidate score of both maps read once, the index
+    set written once."""
+    import numpy as np
+    import torch
+
+    import synth
+    sh = SELECT_SHAPE
+    B, H, L = sh["batch"], sh["n_kv_heads"], sh["score_len"]
+    rng = np.random.Generator(np.random.PCG64(sh["seed"]))
+    ctx_np = np.full(B, L, np.int32)
+    draft_np, target_np = synth.importance_maps(rng, ctx_np, H, L)
+    draft, target = torch.from_numpy(draft_np).to(dev), torch.from_numpy(target_np).to(dev)
+    ctx = torch.from_numpy(ctx_np).to(dev)
+    kv_idx = torch.empty((B, H, sh["n_sel"]), dtype=torch.int32, device=dev)
+    kw = dict(n_sel=sh["n_sel"], n_sink=sh["n_sink"], n_recent=sh["n_recent"],
+              n_draft_top=sh["n_draft_top"], kv_idx=kv_idx)
+    for _ in range(warmup):
+        hsv.hsv_select_kv_idx(draft, target, ctx, **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(steps):
+            hsv.hsv_select_kv_idx(draft, target, ctx, **kw)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    n_cand = L - sh["n_sink"] - sh["n_recent"]
+    nbytes = B * H * (2 * 4 * n_cand + 4 * sh["n_sel"])
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "select_kv_idx (exact radix select, one workgroup per sequence and KV head)",
+            "workload": f"B{B} Hkv{H} L{L} n_sel {sh['n_sel']} (sinks {sh['n_sink']}, "
+                        f"window {sh['n_recent']}, draft top {sh['n_draft_top']})",
+            "kernel_us": round(us, 2), "algorithmic_bytes_per_launch": nbytes,
+            "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +204,8 @@ def main(argv=None) -> int:
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-selection", action="store_true",
+                    help="skip the index-set selection measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
@@ -318,6 +374,9 @@ def main(argv=None) -> int:
                    "graph_ms_per_step_events": round(graph_ms, 5),
                    "eager_ms_per_step": round(eager_ms, 5)},
     }
+    if not args.no_selection:
+        log("bench: timing the index-set selection")
+        result["selection"] = measure_selection(hsv, dev, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

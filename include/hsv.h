@@ -169,6 +169,27 @@ hsv_status hsv_gather_kv(const void *k_cache, const void *v_cache,
                          int32_t head_dim, int32_t n_sel, int32_t dtype,
                          hipStream_t stream);
 
+/* Fixed-size verification index set (Dustin page, methodology 1: hybrid
+ * attention aggregation of a draft-lookahead and a target-historical signal;
+ * the sparse verification attention then reads only these positions).
+ * For each (sequence b, KV head g), of the positions [0, c) with
+ * c = min(ctx_lens[b], score_len): the first n_sink and the last n_recent
+ * are kept; of the positions between them, the n_draft_top best by
+ * draft_score, then the best remaining ones by target_score, until n_sel
+ * positions are chosen.  Best = higher score; NaN ranks below every number;
+ * -0 equals +0; ties go to the lower position.
+ * draft_score, target_score [B, Hkv, score_len] float (entries at or past
+ * c_b are not read); ctx_lens [B] int32 (device); kv_idx [B, Hkv, n_sel]
+ * int32 out, strictly increasing -- if c_b < n_sel the tail is -1.
+ * Requires n_sink + n_recent <= n_sel, n_draft_top >= 0 and
+ * score_len <= 524288; the chosen set is unique (no randomness). */
+hsv_status hsv_select_kv_idx(const float *draft_score, const float *target_score,
+                             int32_t score_len, const int32_t *ctx_lens,
+                             int32_t batch, int32_t n_kv_heads, int32_t n_sel,
+                             int32_t n_sink, int32_t n_recent,
+                             int32_t n_draft_top, int32_t *kv_idx,
+                             hipStream_t stream);
+
 /* Exact log-sum-exp merge of partial attention results (LongSpec section
  * 2.C: the parts' outputs are combined exactly), e.g. partials over disjoint
  * key ranges computed on several devices.

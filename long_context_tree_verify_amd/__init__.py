@@ -206,6 +206,28 @@ def hsv_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype=torc
     return o, lse
 
 
+def hsv_select_kv_idx(draft_score: torch.Tensor, target_score: torch.Tensor,
+                      ctx_lens: torch.Tensor, *, n_sel: int, n_sink: int, n_recent: int,
+                      n_draft_top: int, kv_idx=None, stream=None) -> torch.Tensor:
+    """Verification index set (see include/hsv.h): draft_score, target_score
+    float32 [B, Hkv, L]; returns kv_idx int32 [B, Hkv, n_sel]."""
+    if draft_score.dtype != torch.float32 or target_score.dtype != torch.float32 or \
+            draft_score.dim() != 3 or tuple(target_score.shape) != tuple(draft_score.shape):
+        raise ValueError("draft_score and target_score must be float32 [B, Hkv, L]")
+    B, Hkv, L = draft_score.shape
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("ctx_lens must be int32 [B]")
+    if kv_idx is None:
+        kv_idx = torch.empty((B, Hkv, n_sel), dtype=torch.int32, device=draft_score.device)
+    if kv_idx.dtype != torch.int32 or tuple(kv_idx.shape) != (B, Hkv, n_sel):
+        raise ValueError("kv_idx must be int32 [B, Hkv, n_sel]")
+    _check_dev(draft_score, target_score, ctx_lens, kv_idx)
+    _check(lib.hsv_select_kv_idx(_ptr(draft_score), _ptr(target_score), L, _ptr(ctx_lens), B, Hkv,
+                                 n_sel, n_sink, n_recent, n_draft_top, _ptr(kv_idx),
+                                 _stream(stream, draft_score.device)), "hsv_select_kv_idx")
+    return kv_idx
+
+
 def hsv_status_string(code: int) -> str:
     return _lib.status_string(code)
 

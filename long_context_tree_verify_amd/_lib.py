@@ -35,6 +35,7 @@ EXPORTS = (
     "hsv_tree_ancestor_mask",
     "hsv_gather_kv",
     "hsv_lse_merge",
+    "hsv_select_kv_idx",
     "hsv_status_string",
     "hsv_version",
 )
@@ -68,7 +69,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m long_context_tree_verify_amd.build_lib`")
+            f"{LIB_PATH} is not built; run `python long_context_tree_verify_amd/build_lib.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -79,8 +80,10 @@ def load() -> ctypes.CDLL:
     lib.hsv_tree_ancestor_mask.argtypes = [P, P, i32, i32, P]
     lib.hsv_gather_kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     lib.hsv_lse_merge.argtypes = [P, P, i32, i64, i32, P, P, i32, P]
+    lib.hsv_select_kv_idx.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, i32, P, P]
     for name in ("hsv_verify_workspace_bytes", "hsv_verify_attn", "hsv_verify_attn_sparse",
-                 "hsv_tree_ancestor_mask", "hsv_gather_kv", "hsv_lse_merge"):
+                 "hsv_tree_ancestor_mask", "hsv_gather_kv", "hsv_lse_merge",
+                 "hsv_select_kv_idx"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hsv_status_string.argtypes = [ctypes.c_int]
     lib.hsv_status_string.restype = ctypes.c_char_p

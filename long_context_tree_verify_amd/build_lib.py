@@ -1,6 +1,8 @@
 """Build libhsv.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m long_context_tree_verify_amd.build_lib [--jobs N]
+    python long_context_tree_verify_amd/build_lib.py [--jobs N]
+
+Run it by path: importing the package loads the library this rebuilds.
 """
 
 from __future__ import annotations
@@ -20,7 +22,8 @@ OUT = os.path.join(PKG, "libhsv.so")
 BUILD = os.path.join(ROOT, "_build", "hsv")
 ARCH = "gfx950"
 
-SOURCES = ["hsv_api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_dma.hip", "attn_dma_small.hip", "aux_kernels.hip"]
+SOURCES = ["hsv_api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_dma.hip", "attn_dma_small.hip", "aux_kernels.hip",
+           "select.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -45,6 +45,12 @@ hipError_t launch_tree_mask(const int32_t *parent, uint64_t *anc, int batch, int
 hipError_t launch_gather_kv(const void *k, const void *v, const int32_t *idx, void *k_out,
                             void *v_out, int batch, int hkv, int cap, int head_dim, int n_sel,
                             int elem_bytes, hipStream_t s);
+// Verification index-set selection (one workgroup per (b, kv head)).
+hipError_t launch_select_kv_idx(const float *draft, const float *target, int score_len,
+                                const int32_t *ctx_lens, int batch, int hkv, int n_sel,
+                                int n_sink, int n_recent, int n_draft_top, int32_t *kv_idx,
+                                hipStream_t s);
+int select_max_positions();
 // Device-side precondition check; ORs HSV-internal error bits into p.err.
 hipError_t launch_validate(const Plan &p, hipStream_t s);
 

@@ -18,6 +18,7 @@ from .gen import (  # noqa: F401
     VerifyInputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    importance_maps,
     make_inputs,
     random_tree_parents,
     chain_parents,

@@ -138,6 +138,37 @@ def zipf_index_set(rng: np.random.Generator, ctx: int, n_sel: int, n_sink: int,
     return idx
 
 
+def importance_maps(rng: np.random.Generator, ctx_lens: np.ndarray, n_kv_heads: int,
+                    score_len: int, zipf_a: float = 1.1, noise: float = 0.5):
+    """Synthetic draft-lookahead and target-historical importance maps.
+
+    For each (sequence b, KV head g) the positions [0, ctx_b) get a random rank
+    r (a permutation of 1..ctx_b) and a base weight r ** -zipf_a.  The target
+    map is base * exp(noise * z1), the draft map base ** 0.8 * exp(noise * z2)
+    (z1, z2 independent standard normals), each normalised to sum 1 over the
+    row like an attention-mass map and rounded to bf16 precision (equal values
+    occur, as they do in maps kept at that precision).  Positions at or past
+    ctx_b are NaN: a reader of them is wrong.  Returns (draft, target), float32
+    [B, Hkv, score_len].  Draw order: per (b, g): rank, z1, z2.
+    """
+    B = int(ctx_lens.shape[0])
+    draft = np.full((B, n_kv_heads, score_len), np.nan, dtype=np.float32)
+    target = np.full((B, n_kv_heads, score_len), np.nan, dtype=np.float32)
+    for b in range(B):
+        c = int(min(max(int(ctx_lens[b]), 0), score_len))
+        for g in range(n_kv_heads):
+            rank = rng.permutation(c).astype(np.float64) + 1.0
+            base = rank ** -zipf_a
+            z1 = rng.standard_normal(c)
+            z2 = rng.standard_normal(c)
+            for out, w in ((target, base * np.exp(noise * z1)),
+                           (draft, base ** 0.8 * np.exp(noise * z2))):
+                if c:
+                    w = (w / w.sum()).astype(np.float32)
+                    out[b, g, :c] = bf16_bits_to_f32(f32_to_bf16_bits(w))
+    return draft, target
+
+
 # ----------------------------------------------------------------------------
 # workloads
 # ----------------------------------------------------------------------------

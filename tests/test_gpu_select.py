@@ -1,0 +1,121 @@
+"""GPU parity of the verification index-set selection (Dustin page,
+methodology 1): hsv_select_kv_idx through the C ABI against
+oracle.select_kv_idx, bit-exact.
+
+Cases: the 65536-position, 8 x 8 (sequence, KV head) shape of the sparse
+workload with bf16-precision maps (many equal scores); ragged contexts down
+to 0 and below the budget; NaN, +-0 and +-inf scores; a few distinct values
+only; the corner budgets (no draft share, draft share beyond the budget, no
+sinks or window, budget equal to the context); the largest score row.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from util import log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hsv(gpu):
+    import long_context_tree_verify_amd as m
+    return m
+
+
+def _select(hsv, gpu, draft, target, ctx, **kw):
+    import torch
+    out = hsv.hsv_select_kv_idx(torch.from_numpy(np.ascontiguousarray(draft)).to(gpu),
+                                torch.from_numpy(np.ascontiguousarray(target)).to(gpu),
+                                torch.from_numpy(np.asarray(ctx, np.int32)).to(gpu), **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check(hsv, gpu, draft, target, ctx, what, **kw):
+    got = _select(hsv, gpu, draft, target, ctx, **kw)
+    ref = oracle.select_kv_idx(draft, target, np.asarray(ctx), **kw)
+    bad = np.argwhere((got != ref).any(axis=-1))
+    assert bad.size == 0, f"{what}: (b, g) rows differ: {bad[:4].tolist()}"
+    log(f"  {what}: {got.shape} identical")
+
+
+def test_full_size_importance_maps(hsv, gpu):
+    rng = np.random.Generator(np.random.PCG64(505))
+    ctx = np.full(8, 65536, np.int32)
+    draft, target = synth.importance_maps(rng, ctx, 8, 65536)
+    _check(hsv, gpu, draft, target, ctx, "B8 Hkv8 L65536 n_sel 4096",
+           n_sel=4096, n_sink=4, n_recent=512, n_draft_top=1790)
+
+
+def test_ragged_contexts(hsv, gpu):
+    rng = np.random.Generator(np.random.PCG64(506))
+    ctx = np.array([0, 1, 3, 100, 515, 516, 600, 4095, 4096, 4097, 9000, 20000], np.int32)
+    draft, target = synth.importance_maps(rng, ctx, 3, 20000)
+    _check(hsv, gpu, draft, target, ctx, "ragged", n_sel=4096, n_sink=4, n_recent=512,
+           n_draft_top=1000)
+    _check(hsv, gpu, draft, target, ctx, "ragged, small budget", n_sel=37, n_sink=5,
+           n_recent=7, n_draft_top=11)
+
+
+@pytest.mark.parametrize("m", [0, 1, 50, 10 ** 6])
+def test_draft_share(hsv, gpu, m):
+    rng = np.random.Generator(np.random.PCG64(507 + m % 97))
+    ctx = np.array([3000, 2047, 1025], np.int32)
+    draft, target = synth.importance_maps(rng, ctx, 2, 3000)
+    _check(hsv, gpu, draft, target, ctx, f"n_draft_top {m}", n_sel=300, n_sink=4,
+           n_recent=64, n_draft_top=m)
+
+
+def test_special_values_and_ties(hsv, gpu):
+    rng = np.random.Generator(np.random.PCG64(508))
+    B, H, L = 4, 4, 5000
+    ctx = np.array([5000, 4999, 1234, 77], np.int32)
+    vals = np.array([np.nan, -0.0, 0.0, np.inf, -np.inf, 1.0, -1.0, 2.5, 1e-30, -1e-30],
+                    np.float32)
+    draft = vals[rng.integers(0, vals.size, (B, H, L))]
+    target = vals[rng.integers(0, vals.size, (B, H, L))]
+    _check(hsv, gpu, draft, target, ctx, "special values", n_sel=700, n_sink=3, n_recent=20,
+           n_draft_top=333)
+    few = rng.integers(0, 3, (B, H, L)).astype(np.float32)
+    _check(hsv, gpu, few, few[:, ::-1].copy(), ctx, "three values", n_sel=1500, n_sink=0,
+           n_recent=0, n_draft_top=600)
+    allnan = np.full((B, H, L), np.nan, np.float32)
+    _check(hsv, gpu, allnan, allnan, ctx, "all NaN", n_sel=100, n_sink=2, n_recent=2,
+           n_draft_top=10)
+
+
+def test_budget_corners(hsv, gpu):
+    rng = np.random.Generator(np.random.PCG64(509))
+    ctx = np.array([64, 700, 1024], np.int32)
+    draft, target = synth.importance_maps(rng, ctx, 2, 1024)
+    _check(hsv, gpu, draft, target, ctx, "n_sel = c", n_sel=64, n_sink=4, n_recent=8,
+           n_draft_top=20)
+    _check(hsv, gpu, draft, target, ctx, "sinks + window = budget", n_sel=40, n_sink=8,
+           n_recent=32, n_draft_top=20)
+    _check(hsv, gpu, draft, target, ctx, "budget 1", n_sel=1, n_sink=0, n_recent=1,
+           n_draft_top=0)
+    _check(hsv, gpu, draft, target, ctx, "budget above L", n_sel=2000, n_sink=16, n_recent=16,
+           n_draft_top=5)
+
+
+def test_largest_row(hsv, gpu):
+    L = 1 << 19            # the largest score row the ABI accepts
+    rng = np.random.Generator(np.random.PCG64(510))
+    ctx = np.array([L, L - 12345], np.int32)
+    draft, target = synth.importance_maps(rng, ctx, 1, L)
+    _check(hsv, gpu, draft, target, ctx, f"L {L}", n_sel=8192, n_sink=4, n_recent=1024,
+           n_draft_top=3000)
+
+
+def test_rejects_bad_arguments(hsv, gpu):
+    import torch
+    d = torch.zeros((1, 1, 16), dtype=torch.float32, device=gpu)
+    c = torch.tensor([16], dtype=torch.int32, device=gpu)
+    with pytest.raises(RuntimeError):
+        hsv.hsv_select_kv_idx(d, d, c, n_sel=4, n_sink=3, n_recent=2, n_draft_top=0)
+    big = torch.zeros((1, 1, (1 << 19) + 1), dtype=torch.float32, device=gpu)
+    with pytest.raises(RuntimeError):
+        hsv.hsv_select_kv_idx(big, big, c, n_sel=4, n_sink=0, n_recent=0, n_draft_top=0)
