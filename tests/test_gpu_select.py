@@ -119,3 +119,25 @@ def test_rejects_bad_arguments(hsv, gpu):
     big = torch.zeros((1, 1, (1 << 19) + 1), dtype=torch.float32, device=gpu)
     with pytest.raises(RuntimeError):
         hsv.hsv_select_kv_idx(big, big, c, n_sel=4, n_sink=0, n_recent=0, n_draft_top=0)
+
+
+def test_sample_defeating_map(hsv, gpu):
+    # Rows of 65536 keep 64 keys per thread (position j * 1024 + t) and
+    # sample column j of thread t when j % 16 == (t // 64) % 16.  Here 500
+    # sampled positions hold the only large scores: the floor taken from the
+    # sample leaves fewer than k keys, so the selection must fall back to
+    # every candidate.  A second row puts the large scores off the sample.
+    L = 65536
+    rng = np.random.Generator(np.random.PCG64(511))
+    p = np.arange(L)
+    sampled = np.flatnonzero((p // 1024) % 16 == (p % 1024 // 64) % 16)
+    unsampled = np.setdiff1d(p, sampled)
+    draft = rng.random((2, 1, L), dtype=np.float32)
+    target = rng.random((2, 1, L), dtype=np.float32)
+    for row, pool in ((0, sampled), (1, unsampled)):
+        hot = rng.choice(pool[(pool >= 4) & (pool < L - 512)], 500, replace=False)
+        draft[row, 0, hot] += 1000.0
+        target[row, 0, hot] += 1000.0
+    ctx = np.array([L, L], np.int32)
+    _check(hsv, gpu, draft, target, ctx, "sample-defeating", n_sel=4096, n_sink=4,
+           n_recent=512, n_draft_top=1790)
