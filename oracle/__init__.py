@@ -231,3 +231,74 @@ def recall_rate(lse_subset: np.ndarray, lse_full: np.ndarray) -> np.ndarray:
     (the pages name the rate without defining it; this is the plain
     reading)."""
     return np.exp(np.asarray(lse_subset, dtype=np.float64) - np.asarray(lse_full, np.float64))
+
+
+def tree_depth(parent: np.ndarray) -> np.ndarray:
+    """Depth of each draft node, counting the node itself: a child of the
+    cached prefix (parent -1) has depth 1, its children depth 2, and so on
+    (LongSpec section 2.C: draft tokens form a tree rooted at the prefix).
+    Sequences whose parent array is invalid (an entry outside [-1, i-1])
+    get -1 everywhere."""
+    parent = np.atleast_2d(np.asarray(parent, dtype=np.int64))
+    B, N = parent.shape
+    depth = np.full((B, N), -1, dtype=np.int64)
+    for b in range(B):
+        if any(not (-1 <= parent[b, i] <= i - 1) for i in range(N)):
+            continue
+        for i in range(N):
+            p = parent[b, i]
+            depth[b, i] = 1 if p < 0 else depth[b, p] + 1
+    return depth
+
+
+def tree_position_ids(parent: np.ndarray, ctx_lens: np.ndarray) -> np.ndarray:
+    """Sequence position of each draft node, ctx_b + depth(i) - 1: the node
+    takes the place it would have in the sequence if its branch were
+    accepted (the position a rotary embedding uses).  -1 for every node of
+    a sequence with an invalid parent array.  int32 [B, N]."""
+    depth = tree_depth(parent)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)[:, None]
+    return np.where(depth < 0, -1, ctx + depth - 1).astype(np.int32)
+
+
+def accepted_path(parent: np.ndarray, node: int) -> np.ndarray:
+    """Nodes from the root's child down to `node`, in that order (empty for
+    node -1).  Parents precede children, so this is the ancestor-or-self set
+    of `node` in increasing index order."""
+    path = []
+    while node >= 0:
+        path.append(int(node))
+        node = int(parent[node])
+    return np.array(path[::-1], dtype=np.int64)
+
+
+def accept_path(k: np.ndarray, v: np.ndarray, ctx_lens: np.ndarray, parent: np.ndarray,
+                accept_node: np.ndarray):
+    """KV-cache update after verification: the accepted draft tokens join the
+    cache and the rejected ones are dropped (HiSpec page, KV and hidden-state
+    reuse; Dustin page, verification workflow step 5).
+
+    k, v [B, Hkv, S_cap, D] hold the draft tree's rows at [c_b, c_b + N).
+    For each sequence b with accept_node[b] = a >= 0, the path
+    p_0 < p_1 < ... < p_{L-1} = a (root side first) is moved so that row
+    c_b + t receives what row c_b + p_t held, for t < L; c_b becomes
+    c_b + L.  Rows at c_b + L and beyond keep whatever they held.  A
+    sequence with accept_node -1 (nothing accepted), an invalid parent array,
+    accept_node outside [-1, N) or c_b + N > S_cap is left unchanged.
+    Returns new (k, v, ctx_lens) arrays; the inputs are not modified."""
+    k2, v2 = np.array(k, copy=True), np.array(v, copy=True)
+    ctx2 = np.array(ctx_lens, dtype=np.int32, copy=True)
+    parent = np.atleast_2d(np.asarray(parent, dtype=np.int64))
+    B, N = parent.shape
+    S = k.shape[2]
+    depth = tree_depth(parent)
+    for b in range(B):
+        a = int(accept_node[b])
+        c = int(ctx_lens[b])
+        if a < 0 or a >= N or depth[b, 0] < 0 or c < 0 or c + N > S:
+            continue
+        path = accepted_path(parent[b], a)
+        k2[b, :, c:c + path.size] = k[b][:, c + path]
+        v2[b, :, c:c + path.size] = v[b][:, c + path]
+        ctx2[b] = c + path.size
+    return k2, v2, ctx2
