@@ -169,6 +169,36 @@ hsv_status hsv_gather_kv(const void *k_cache, const void *v_cache,
                          int32_t head_dim, int32_t n_sel, int32_t dtype,
                          hipStream_t stream);
 
+/* Sequence position of each draft node (LongSpec section 2.C: the draft
+ * tokens form a tree rooted at the cached prefix): pos_ids[b, i] =
+ * ctx_lens[b] + depth(i) - 1, where a child of the prefix (parent -1) has
+ * depth 1 -- the position node i would take if its branch were accepted, as
+ * a rotary embedding needs it.  parent [B, N] int32 in [-1, i-1]; ctx_lens
+ * [B] int32; pos_ids [B, N] int32 out.  N in [1, 64].  Every entry of a
+ * sequence with an out-of-range parent is written as -1. */
+hsv_status hsv_tree_position_ids(const int32_t *parent, const int32_t *ctx_lens,
+                                 int32_t *pos_ids, int32_t batch, int32_t n_draft,
+                                 hipStream_t stream);
+
+/* Cache update after verification (HiSpec page, reuse of the KV cache with
+ * the entries of rejected tokens removed; Dustin page, verification
+ * workflow step 5: accepted tokens join the cache, rejected ones are
+ * dropped).  k_cache, v_cache [B, Hkv, S_cap, D] (dtype HSV_F32 or
+ * HSV_BF16, D 64 or 128) hold the draft tree's rows at [c_b, c_b + N),
+ * c_b = ctx_lens[b].  For accept_node[b] = a in [0, N), the path
+ * p_0 < ... < p_{L-1} = a from the prefix down to a is moved in place so
+ * that row c_b + t holds what row c_b + p_t held, and ctx_lens[b] becomes
+ * c_b + L; rows at c_b + L and beyond are not written.  accept_node -1
+ * accepts nothing.  A sequence with accept_node outside [-1, N), an
+ * out-of-range parent, c_b < 0 or c_b + N > S_cap is left unchanged.
+ * ctx_lens is read and updated on the device (stream-ordered: two
+ * launches); parent [B, N] and accept_node [B] are int32.  N in [1, 64]. */
+hsv_status hsv_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens,
+                           const int32_t *parent, const int32_t *accept_node,
+                           int32_t batch, int32_t n_kv_heads, int32_t kv_capacity,
+                           int32_t head_dim, int32_t n_draft, int32_t dtype,
+                           hipStream_t stream);
+
 /* Fixed-size verification index set (Dustin page, methodology 1: hybrid
  * attention aggregation of a draft-lookahead and a target-historical signal;
  * the sparse verification attention then reads only these positions).

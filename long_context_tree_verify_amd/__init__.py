@@ -228,6 +228,44 @@ def hsv_select_kv_idx(draft_score: torch.Tensor, target_score: torch.Tensor,
     return kv_idx
 
 
+def hsv_tree_position_ids(parent: torch.Tensor, ctx_lens: torch.Tensor,
+                          pos_ids: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Sequence position c_b + depth(i) - 1 of each draft node (int32 [B, N])."""
+    if parent.dtype != torch.int32 or parent.dim() != 2:
+        raise ValueError("parent must be int32 [B, N]")
+    B, N = parent.shape
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("ctx_lens must be int32 [B]")
+    if pos_ids is None:
+        pos_ids = torch.empty((B, N), dtype=torch.int32, device=parent.device)
+    if pos_ids.dtype != torch.int32 or tuple(pos_ids.shape) != (B, N):
+        raise ValueError("pos_ids must be int32 [B, N]")
+    _check_dev(parent, ctx_lens, pos_ids)
+    _check(lib.hsv_tree_position_ids(_ptr(parent), _ptr(ctx_lens), _ptr(pos_ids), B, N,
+                                     _stream(stream, parent.device)), "hsv_tree_position_ids")
+    return pos_ids
+
+
+def hsv_accept_path(k_cache: torch.Tensor, v_cache: torch.Tensor, ctx_lens: torch.Tensor,
+                    parent: torch.Tensor, accept_node: torch.Tensor, stream=None) -> None:
+    """In-place cache update: the accepted node's path moves to [c_b, c_b + L)
+    and ctx_lens grows by L (see include/hsv.h)."""
+    B, Hkv, cap, D = k_cache.shape
+    dt = _dtype_code(k_cache, "k_cache")
+    if v_cache.dtype != k_cache.dtype or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache must match k_cache")
+    if parent.dtype != torch.int32 or parent.dim() != 2 or parent.shape[0] != B:
+        raise ValueError("parent must be int32 [B, N]")
+    N = parent.shape[1]
+    for name, t in (("ctx_lens", ctx_lens), ("accept_node", accept_node)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,):
+            raise ValueError(f"{name} must be int32 [B]")
+    _check_dev(k_cache, v_cache, ctx_lens, parent, accept_node)
+    _check(lib.hsv_accept_path(_ptr(k_cache), _ptr(v_cache), _ptr(ctx_lens), _ptr(parent),
+                               _ptr(accept_node), B, Hkv, cap, D, N, dt,
+                               _stream(stream, k_cache.device)), "hsv_accept_path")
+
+
 def hsv_status_string(code: int) -> str:
     return _lib.status_string(code)
 

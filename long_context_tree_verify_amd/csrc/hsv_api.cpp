@@ -328,6 +328,33 @@ hsv_status hsv_select_kv_idx(const float *draft_score, const float *target_score
              : HSV_ERR_HIP;
 }
 
+hsv_status hsv_tree_position_ids(const int32_t *parent, const int32_t *ctx_lens,
+                                 int32_t *pos_ids, int32_t batch, int32_t n_draft,
+                                 hipStream_t stream) {
+  if (!parent || !ctx_lens || !pos_ids) return HSV_ERR_NULL;
+  if (batch < 1 || n_draft < 1 || n_draft > 64) return HSV_ERR_SHAPE;
+  return launch_tree_position_ids(parent, ctx_lens, pos_ids, batch, n_draft, stream) == hipSuccess
+             ? HSV_OK
+             : HSV_ERR_HIP;
+}
+
+hsv_status hsv_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens, const int32_t *parent,
+                           const int32_t *accept_node, int32_t batch, int32_t n_kv_heads,
+                           int32_t kv_capacity, int32_t head_dim, int32_t n_draft, int32_t dtype,
+                           hipStream_t stream) {
+  if (!k_cache || !v_cache || !ctx_lens || !parent || !accept_node) return HSV_ERR_NULL;
+  if (dtype != HSV_F32 && dtype != HSV_BF16) return HSV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return HSV_ERR_UNSUPPORTED;
+  if (batch < 1 || n_kv_heads < 1 || n_draft < 1 || n_draft > 64 || kv_capacity < n_draft)
+    return HSV_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * n_kv_heads > (int64_t{1} << 31) - 1) return HSV_ERR_SHAPE;
+  const int row_bytes = head_dim * (dtype == HSV_F32 ? 4 : 2);
+  return launch_accept_path(k_cache, v_cache, ctx_lens, parent, accept_node, batch, n_kv_heads,
+                            kv_capacity, row_bytes, n_draft, stream) == hipSuccess
+             ? HSV_OK
+             : HSV_ERR_HIP;
+}
+
 hsv_status hsv_lse_merge(const float *o_parts, const float *lse_parts, int32_t n_parts,
                          int64_t n_rows, int32_t head_dim, void *o, float *lse, int32_t out_dtype,
                          hipStream_t stream) {

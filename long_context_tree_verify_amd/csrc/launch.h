@@ -51,6 +51,12 @@ hipError_t launch_select_kv_idx(const float *draft, const float *target, int sco
                                 int n_sink, int n_recent, int n_draft_top, int32_t *kv_idx,
                                 hipStream_t s);
 int select_max_positions();
+// Tree position ids and the accepted-path cache update.
+hipError_t launch_tree_position_ids(const int32_t *parent, const int32_t *ctx_lens,
+                                    int32_t *pos_ids, int batch, int n_draft, hipStream_t s);
+hipError_t launch_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens,
+                              const int32_t *parent, const int32_t *accept_node, int batch,
+                              int hkv, int s_cap, int row_bytes, int n_draft, hipStream_t s);
 // Device-side precondition check; ORs HSV-internal error bits into p.err.
 hipError_t launch_validate(const Plan &p, hipStream_t s);
 
