@@ -104,7 +104,6 @@ def recorded_traffic(workload: str):
 def cpu_baseline(inp, target_s: float):
     """Time the fp64 oracle on a bounded sample of output rows and scale."""
     import numpy as np
-    import oracle
     wl = inp.wl
     B, N, Hq = wl.batch, wl.n_draft, wl.n_q_heads
     total = B * N * Hq
@@ -193,6 +192,66 @@ def measure_selection(hsv, dev, steps: int, warmup: int):
             "kernel_us": round(us, 2), "algorithmic_bytes_per_launch": nbytes,
             "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def measure_accept(hsv, dev, inp, steps: int):
+    """Accepted-path cache update on the workload's own shape and trees, the
+    deepest node of each tree accepted.  The context lengths are restored
+    before every call (the update grows them); HIP events on the current
+    stream bracket each call alone.  Bytes: every moved K and V row read
+    and written once."""
+    import numpy as np
+    import torch
+
+    wl = inp.wl
+    B, H, N, D = wl.batch, wl.n_kv_heads, wl.n_draft, wl.head_dim
+    S = wl.kv_capacity
+    dt = torch.bfloat16 if inp.is_bf16 else torch.float32
+    k = torch.zeros((B, H, S, D), dtype=dt, device=dev)
+    v = torch.zeros_like(k)
+    parent = torch.from_numpy(inp.parent).to(dev)
+    # the path of node i is its ancestor-or-self mask; the deepest node has
+    # the most bits; rows 0, 1, ... at the path's start are already in place
+    anc = hsv.hsv_tree_ancestor_mask(parent).cpu().numpy().view(np.uint64)
+    bits = np.array([[bin(int(x)).count("1") for x in row] for row in anc])
+    node_np = bits.argmax(axis=1).astype(np.int32)
+    node = torch.from_numpy(node_np).to(dev)
+    ctx0 = torch.from_numpy(inp.ctx_lens).to(dev)
+    ctx = ctx0.clone()
+    moved = 0
+    for b in range(B):
+        m = int(anc[b, node_np[b]])
+        lead = (~m & (m + 1)).bit_length() - 1      # trailing ones of m
+        moved += bin(m).count("1") - lead
+    nbytes = 2 * 2 * moved * H * D * k.element_size()
+    # K (restore lengths, update) pairs in one graph, less a graph of the K
+    # restores alone; HIP events on the capture stream bracket each replay
+    side = torch.cuda.Stream(dev)
+
+    def timed(with_update):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(steps):
+                ctx.copy_(ctx0)
+                if with_update:
+                    hsv.hsv_accept_path(k, v, ctx, parent, node)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us = max(timed(True) - timed(False), 1e-3)
+    return {"kernel": "accept_copy + accept_bump (one workgroup per sequence and KV head)",
+            "workload": f"{wl.name} shape, deepest node accepted: {moved} rows moved per KV head",
+            "call_us": round(us, 2), "algorithmic_bytes_per_call": nbytes,
+            "achieved": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s",
+            "note": "two launches (copy, then the length update), timed in a graph; "
+                    "launch-bound at this size"}
 
 
 def main(argv=None) -> int:
@@ -374,6 +433,8 @@ def main(argv=None) -> int:
                    "graph_ms_per_step_events": round(graph_ms, 5),
                    "eager_ms_per_step": round(eager_ms, 5)},
     }
+    log("bench: timing the accepted-path cache update")
+    result["accept"] = measure_accept(hsv, dev, inp, args.steps)
     if not args.no_selection:
         log("bench: timing the index-set selection")
         result["selection"] = measure_selection(hsv, dev, args.steps, args.warmup)

@@ -17,6 +17,8 @@ from .gen import (  # noqa: F401
     Workload,
     VerifyInputs,
     bf16_bits_to_f32,
+    block_masks,
+    random_masks,
     f32_to_bf16_bits,
     importance_maps,
     make_inputs,

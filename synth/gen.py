@@ -100,6 +100,29 @@ def random_tree_parents(rng: np.random.Generator, n: int, max_depth: int,
     return parent
 
 
+def block_masks(n: int, block: int) -> np.ndarray:
+    """Visibility masks of block-parallel drafting (FlexDraft page, attention
+    tuning): the n draft tokens form consecutive blocks of `block` tokens;
+    a token sees every token of its own block, earlier and later ones alike,
+    and none of the other blocks.  uint64 [n], bit j = token j visible."""
+    if not 1 <= n <= 64:
+        raise ValueError("at most 64 draft tokens per mask word")
+    blk = np.arange(n) // block
+    out = np.zeros(n, dtype=np.uint64)
+    for i in range(n):
+        for j in np.flatnonzero(blk == blk[i]):
+            out[i] |= np.uint64(1) << np.uint64(j)
+    return out
+
+
+def random_masks(rng: np.random.Generator, batch: int, n: int, density: float = 0.5):
+    """Arbitrary visibility masks: each bit j < n set with probability
+    `density`.  uint64 [batch, n]."""
+    bits = rng.random((batch, n, n)) < density
+    weights = np.uint64(1) << np.arange(n, dtype=np.uint64)
+    return (bits.astype(np.uint64) * weights).sum(axis=2, dtype=np.uint64)
+
+
 def zipf_ranked_draw(rng: np.random.Generator, m: int, n_draw: int, zipf_a: float):
     """Draw ``n_draw`` of ``m`` positions without replacement, P ~ rank**-a.
 
