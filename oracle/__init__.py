@@ -174,6 +174,24 @@ def gather_kv(k: np.ndarray, v: np.ndarray, kv_idx: np.ndarray):
     return k[bi, gi, kv_idx], v[bi, gi, kv_idx]
 
 
+def paged_to_contiguous(k_pool: np.ndarray, v_pool: np.ndarray, table: np.ndarray):
+    """Contiguous cache of a paged one (HiSpec page: paged attention with
+    block tables): row t of sequence b, head g is row t % bs of pool block
+    table[b, t // bs].  k_pool, v_pool [n_blocks, Hkv, bs, D]; table
+    [B, nb] -> k, v [B, Hkv, nb * bs, D].  Attention over a paged cache is
+    attention over this one."""
+    n_pool, H, bs, D = k_pool.shape
+    B, nb = table.shape
+    out = []
+    for pool in (k_pool, v_pool):
+        x = np.empty((B, H, nb * bs, D), dtype=pool.dtype)
+        for b in range(B):
+            for j in range(nb):
+                x[b, :, j * bs:(j + 1) * bs] = pool[table[b, j]]
+        out.append(x)
+    return out[0], out[1]
+
+
 def _top_positions(scores: np.ndarray, pos: np.ndarray, k: int) -> np.ndarray:
     """The k best positions: higher score first, NaN below every number,
     -0 equal to +0, ties to the lower position."""

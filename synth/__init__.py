@@ -23,6 +23,7 @@ from .gen import (  # noqa: F401
     importance_maps,
     make_inputs,
     random_tree_parents,
+    to_paged,
     chain_parents,
     uniform_parents,
     zipf_index_set,

@@ -192,6 +192,35 @@ def importance_maps(rng: np.random.Generator, ctx_lens: np.ndarray, n_kv_heads: 
     return draft, target
 
 
+def to_paged(k: np.ndarray, v: np.ndarray, block_size: int, rng: np.random.Generator,
+             spare_blocks: int = 3):
+    """Lay a contiguous cache [B, Hkv, S_cap, D] out as a paged pool
+    [n_blocks, Hkv, block_size, D] with a block table [B, S_cap / block_size]
+    (HiSpec page: paged attention with block tables).  Logical block j of
+    sequence b goes to pool block table[b, j]; the pool order is a seeded
+    random permutation, and `spare_blocks` extra pool blocks that no table
+    entry names are filled with NaN (a kernel reading them fails parity).
+    Returns (k_pool, v_pool, table)."""
+    B, H, S, D = k.shape
+    if S % block_size:
+        raise ValueError("capacity must be a whole number of blocks")
+    nb = S // block_size
+    n_pool = B * nb + spare_blocks
+    perm = rng.permutation(n_pool)
+    table = perm[:B * nb].reshape(B, nb).astype(np.int32)
+    pools = []
+    for src in (k, v):
+        pool = np.empty((n_pool, H, block_size, D), dtype=src.dtype)
+        if src.dtype == np.uint16:
+            pool[...] = BF16_NAN
+        else:
+            pool[...] = np.nan
+        blocks = src.reshape(B, H, nb, block_size, D).transpose(0, 2, 1, 3, 4)
+        pool[table.reshape(-1)] = blocks.reshape(B * nb, H, block_size, D)
+        pools.append(pool)
+    return pools[0], pools[1], table
+
+
 # ----------------------------------------------------------------------------
 # workloads
 # ----------------------------------------------------------------------------
