@@ -118,6 +118,9 @@ typedef struct hsv_verify_desc {
                        /* one part for the draft tree.  Results do not depend  */
                        /* on the split count beyond rounding.                  */
   uint32_t flags;      /* HSV_FLAG_* bits                                       */
+  int32_t block_size;  /* hsv_verify_attn_paged: tokens per pool block, a power */
+                       /* of two >= 64 dividing kv_capacity; 0 for the other    */
+                       /* calls                                                 */
 } hsv_verify_desc;
 
 /* Bytes of workspace hsv_verify_attn / hsv_verify_attn_sparse need for `d`.
@@ -148,6 +151,30 @@ hsv_status hsv_verify_attn_sparse(const hsv_verify_desc *d, const void *q,
                                   const int32_t *kv_idx, void *o, float *lse,
                                   void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/* Dense verification attention over a paged cache (HiSpec page: paged
+ * attention with block tables, so that sequences of a batch can accept
+ * different numbers of tokens without padding).  Same computation as
+ * hsv_verify_attn on the cache whose row t of sequence b, KV head g is row
+ * t % bs of pool block block_table[b, t / bs], bs = d->block_size:
+ *   k_pool, v_pool [n_pool_blocks, Hkv, bs, D]  (bf16, D = 128)
+ *   block_table    [B, kv_capacity / bs] int32 in [0, n_pool_blocks)
+ * Logical rows [0, c_b) are the prefix and [c_b, c_b + N) the draft tree,
+ * as in the contiguous cache; every table entry those rows fall in must name
+ * a pool block (an entry outside the pool is clamped into it, which gives
+ * wrong values but reads no memory outside the pool; HSV_FLAG_VALIDATE
+ * reports it as HSV_ERR_DEVICE_CHECK).  Runs where the contiguous call
+ * would use the 16-byte DMA kernels (bf16, D = 128, at most 32 or more than
+ * 128 grouped rows); other shapes, HSV_FLAG_NO_PREFIX and more than
+ * 256 * 32 * bs keys return HSV_ERR_UNSUPPORTED.  The workspace size comes
+ * from hsv_verify_workspace_bytes with the same descriptor. */
+hsv_status hsv_verify_attn_paged(const hsv_verify_desc *d, const void *q,
+                                 const void *k_pool, const void *v_pool,
+                                 const int32_t *block_table, int32_t n_pool_blocks,
+                                 const int32_t *ctx_lens, const int32_t *parent,
+                                 const uint64_t *anc_mask, void *o, float *lse,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /* Ancestor bitmask of each draft tree (LongSpec section 2.C: the mask of the
  * speculative part follows the branches of the tree).

@@ -72,9 +72,10 @@ def _check(code: int, where: str):
 
 def make_desc(*, batch, n_draft, n_q_heads, n_kv_heads, head_dim, kv_capacity, max_ctx,
               n_sel=0, in_dtype=HSV_BF16, out_dtype=HSV_F32, scale=0.0, num_splits=0,
-              flags=0) -> HsvVerifyDesc:
+              flags=0, block_size=0) -> HsvVerifyDesc:
     return HsvVerifyDesc(batch, n_draft, n_q_heads, n_kv_heads, head_dim, kv_capacity, max_ctx,
-                         n_sel, in_dtype, out_dtype, float(scale), num_splits, flags)
+                         n_sel, in_dtype, out_dtype, float(scale), num_splits, flags,
+                         block_size)
 
 
 def hsv_verify_workspace_bytes(desc: HsvVerifyDesc) -> int:
@@ -154,6 +155,56 @@ def hsv_verify_attn_sparse(q, k_cache, v_cache, ctx_lens, parent=None, anc_mask=
     return _verify(True, q, k_cache, v_cache, ctx_lens, parent, anc_mask, kv_idx,
                    max_ctx=max_ctx, out_dtype=out_dtype, scale=scale, num_splits=num_splits,
                    flags=flags, o=o, lse=lse, workspace=workspace, stream=stream)
+
+
+def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                          block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                          parent: Optional[torch.Tensor] = None,
+                          anc_mask: Optional[torch.Tensor] = None, *, max_ctx: int,
+                          out_dtype=torch.float32, scale: float = 0.0, num_splits: int = 0,
+                          flags: int = 0, o=None, lse=None, workspace=None, stream=None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Dense verification attention over a paged cache (see include/hsv.h):
+    k_pool, v_pool [n_blocks, Hkv, block_size, D]; block_table int32
+    [B, max_blocks].  Returns (o, lse)."""
+    B, N, Hq, D = q.shape
+    n_pool, Hkv, bs, Dk = k_pool.shape
+    if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("q / k_pool / v_pool shapes disagree")
+    in_dt = _dtype_code(q, "q")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q, k_pool and v_pool must share a dtype")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("ctx_lens must be int32 [B]")
+    if parent is not None and (parent.dtype != torch.int32 or tuple(parent.shape) != (B, N)):
+        raise ValueError("parent must be int32 [B, N]")
+    if anc_mask is not None and (anc_mask.dtype not in (torch.int64, torch.uint64)
+                                 or tuple(anc_mask.shape) != (B, N)):
+        raise ValueError("anc_mask must be 64-bit [B, N]")
+    if o is None:
+        o = torch.empty((B, N, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
+    out_dt = _dtype_code(o, "o")
+    if tuple(o.shape) != (B, N, Hq, D) or lse.dtype != torch.float32 or \
+            tuple(lse.shape) != (B, N, Hq):
+        raise ValueError("o must be [B, N, Hq, D] and lse float32 [B, N, Hq]")
+    desc = make_desc(batch=B, n_draft=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                     kv_capacity=block_table.shape[1] * bs, max_ctx=int(max_ctx), in_dtype=in_dt,
+                     out_dtype=out_dt, scale=scale, num_splits=num_splits, flags=flags,
+                     block_size=bs)
+    need = hsv_verify_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_dev(q, k_pool, v_pool, block_table, ctx_lens, parent, anc_mask, o, lse, workspace)
+    _check(lib.hsv_verify_attn_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                     _ptr(block_table), n_pool, _ptr(ctx_lens), _ptr(parent),
+                                     _ptr(anc_mask), _ptr(o), _ptr(lse), _ptr(workspace),
+                                     ctypes.c_size_t(workspace.numel()),
+                                     _stream(stream, q.device)), "hsv_verify_attn_paged")
+    return o, lse
 
 
 def hsv_tree_ancestor_mask(parent: torch.Tensor, anc_mask: Optional[torch.Tensor] = None,

@@ -32,6 +32,7 @@ EXPORTS = (
     "hsv_verify_workspace_bytes",
     "hsv_verify_attn",
     "hsv_verify_attn_sparse",
+    "hsv_verify_attn_paged",
     "hsv_tree_ancestor_mask",
     "hsv_gather_kv",
     "hsv_lse_merge",
@@ -58,6 +59,7 @@ class HsvVerifyDesc(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("block_size", ctypes.c_int32),
     ]
 
 
@@ -79,6 +81,7 @@ def load() -> ctypes.CDLL:
     lib.hsv_verify_workspace_bytes.argtypes = [D, ctypes.POINTER(sz)]
     lib.hsv_verify_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, sz, P]
     lib.hsv_verify_attn_sparse.argtypes = [D, P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.hsv_verify_attn_paged.argtypes = [D, P, P, P, P, i32, P, P, P, P, P, P, sz, P]
     lib.hsv_tree_ancestor_mask.argtypes = [P, P, i32, i32, P]
     lib.hsv_gather_kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     lib.hsv_lse_merge.argtypes = [P, P, i32, i64, i32, P, P, i32, P]
@@ -86,7 +89,7 @@ def load() -> ctypes.CDLL:
     lib.hsv_tree_position_ids.argtypes = [P, P, P, i32, i32, P]
     lib.hsv_accept_path.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     for name in ("hsv_verify_workspace_bytes", "hsv_verify_attn", "hsv_verify_attn_sparse",
-                 "hsv_tree_ancestor_mask", "hsv_gather_kv", "hsv_lse_merge",
+                 "hsv_verify_attn_paged", "hsv_tree_ancestor_mask", "hsv_gather_kv", "hsv_lse_merge",
                  "hsv_select_kv_idx", "hsv_tree_position_ids", "hsv_accept_path"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hsv_status_string.argtypes = [ctypes.c_int]

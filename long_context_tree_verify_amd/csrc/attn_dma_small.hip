@@ -145,9 +145,32 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   // this wave's blocks: i = wave, wave + 4, ...
   const int my_n = wave < n_blocks ? (n_blocks - wave + kWaves - 1) / kWaves : 0;
 
-  const int64_t kv_row0 = static_cast<int64_t>(bg) * P.cap;
+  const bool paged = !SPARSE && P.block_table != nullptr;
+  const int64_t kv_row0 = paged ? 0 : static_cast<int64_t>(bg) * P.cap;
   const char *kbytes = static_cast<const char *>(P.k) + kv_row0 * kRowBytes;
   const char *vbytes = static_cast<const char *>(P.v) + kv_row0 * kRowBytes;
+  // Paged cache (dense only): lane l holds the pool block of logical block
+  // lb0 + l (a slot spans at most 33 blocks; 32-key blocks start at
+  // multiples of 32 and pool blocks hold a power of two >= 64 rows, so a
+  // key block lies in one pool block).  Entries outside the pool are
+  // clamped into it.
+  int lb0 = 0, ptab = 0;
+  if (paged) {
+    lb0 = t_begin >> P.block_shift;
+    const int lb = lb0 + lane;
+    const int nlb = ((t_end - 1) >> P.block_shift) - lb0 + 1;
+    const int e = (lane < nlb && lb < P.max_blocks)
+                      ? P.block_table[static_cast<int64_t>(b) * P.max_blocks + lb]
+                      : 0;
+    ptab = min(max(e, 0), P.n_pool_blocks - 1);
+  }
+  auto block_off = [&](const int row_first) -> int64_t {
+    if (!paged) return static_cast<int64_t>(row_first) * kRowBytes;
+    const int phys = __builtin_amdgcn_readlane(ptab, (row_first >> P.block_shift) - lb0);
+    const int in_blk = row_first & ((1 << P.block_shift) - 1);
+    return ((static_cast<int64_t>(phys) * P.Hkv + g) * (int64_t{1} << P.block_shift) + in_blk) *
+           kRowBytes;
+  };
   lds_char *const lds = (lds_char *)(smem);
   const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave * kWaveLds;
 
@@ -216,8 +239,9 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     }
     const int row_first = t_begin + (wave + kWaves * k) * kBK;
     const int lim = row_last - row_first;  // last valid key of the block
-    const char *kt = kbytes + static_cast<int64_t>(row_first) * kRowBytes;
-    const char *vt = vbytes + static_cast<int64_t>(row_first) * kRowBytes;
+    const int64_t off = block_off(row_first);
+    const char *kt = kbytes + off;
+    const char *vt = vbytes + off;
     const uint32_t st = ring0 + (k & 1) * kBlockBytes;
     if (lim >= kBK - 1) {
 #pragma unroll

@@ -235,6 +235,13 @@ __global__ __launch_bounds__(256) void validate_kernel(Plan P) {
       if (t < 0 || t >= c || (s > 0 && row[s - 1] >= t)) bits |= kErrIndex;
     }
   }
+  if (P.block_table && c >= 0 && static_cast<int64_t>(c) + P.N <= P.cap) {
+    const int nb = (c + P.N + (1 << P.block_shift) - 1) >> P.block_shift;
+    for (int j = threadIdx.x; j < nb; j += blockDim.x) {
+      const int e = P.block_table[static_cast<int64_t>(b) * P.max_blocks + j];
+      if (e < 0 || e >= P.n_pool_blocks) bits |= kErrIndex;
+    }
+  }
   if (bits) atomicOr(P.err, bits);
 }
 

@@ -25,6 +25,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 hsv_status check_desc(const hsv_verify_desc *d, bool sparse) {
   if (!d) return HSV_ERR_NULL;
+  if (d->block_size != 0) {
+    const int bs = d->block_size;
+    if (bs < 64 || bs > (1 << 20) || (bs & (bs - 1)) || d->kv_capacity % bs) return HSV_ERR_SHAPE;
+    if (sparse || (d->flags & HSV_FLAG_NO_PREFIX)) return HSV_ERR_UNSUPPORTED;
+  }
   if (d->batch < 1 || d->n_draft < 1 || d->n_draft > 64) return HSV_ERR_SHAPE;
   if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads) return HSV_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return HSV_ERR_UNSUPPORTED;
@@ -119,6 +124,8 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
   p->has_prefix = with_prefix;
   p->has_tree = with_tree;
   p->unified = p->kernel == kKernDma256 || p->kernel == kKernDmaSmall;
+  const bool paged = d->block_size > 0;
+  if (paged && !p->unified) return HSV_ERR_UNSUPPORTED;
   if (p->unified) {
     // One key range per (b, kv head): prefix (or index set) then draft rows.  One workgroup
     // per CU: as many splits as fit in one round of the CUs (splits of a
@@ -135,8 +142,17 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
       if (p->B > 1)
         while (ceil_div(keys, target * tile) > 64 && target * 2 <= kMaxSplits) target *= 2;
     }
+    // Paged: splits of whole 64-key tiles (a tile then lies in one pool
+    // block) spanning at most 33 pool blocks (one table entry per lane).
+    int64_t quantum = 32;
+    if (paged) {
+      quantum = 64;
+      target = std::max<int64_t>(target, ceil_div(keys, 32 * static_cast<int64_t>(d->block_size)));
+      if (target > kMaxSplits) return HSV_ERR_UNSUPPORTED;
+    }
     target = std::max<int64_t>(1, std::min<int64_t>(target, kMaxSplits));
-    const int64_t kps = std::max<int64_t>(32, ceil_div(ceil_div(keys, target), 32) * 32);
+    const int64_t kps =
+        std::max<int64_t>(quantum, ceil_div(ceil_div(keys, target), quantum) * quantum);
     p->keys_per_split = static_cast<int32_t>(kps);
     p->n_splits = keys > 0 ? static_cast<int32_t>(ceil_div(keys, kps)) : 0;
     p->tree_slot = -1;
@@ -198,8 +214,13 @@ void carve_workspace(Plan *p, void *ws) {
 hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, const void *k,
                       const void *v, const int32_t *ctx_lens, const int32_t *parent,
                       const uint64_t *anc, const int32_t *kv_idx, void *o, float *lse, void *ws,
-                      size_t ws_bytes, hipStream_t stream) {
+                      size_t ws_bytes, hipStream_t stream, const int32_t *block_table = nullptr,
+                      int32_t n_pool_blocks = 0) {
   if (!d) return HSV_ERR_NULL;
+  // a contiguous call must not carry a block size (the paged entry point
+  // passes the table)
+  if (!block_table && d->block_size != 0) return HSV_ERR_SHAPE;
+  if (block_table && n_pool_blocks < 1) return HSV_ERR_SHAPE;
   Plan p;
   size_t need = 0;
   hsv_status st = make_plan(d, sparse, &p, &need);
@@ -221,6 +242,12 @@ hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, cons
   p.parent = with_tree ? parent : nullptr;
   p.anc = with_tree ? anc : nullptr;
   p.kv_idx = sparse ? kv_idx : nullptr;
+  if (block_table) {
+    p.block_table = block_table;
+    p.block_shift = __builtin_ctz(static_cast<unsigned>(d->block_size));
+    p.max_blocks = d->kv_capacity / d->block_size;
+    p.n_pool_blocks = n_pool_blocks;
+  }
   p.o = o;
   p.lse = lse;
   carve_workspace(&p, ws);
@@ -282,6 +309,19 @@ hsv_status hsv_verify_attn_sparse(const hsv_verify_desc *d, const void *q, const
                                   size_t workspace_bytes, hipStream_t stream) {
   return run_verify(d, true, q, k_cache, v_cache, ctx_lens, parent, anc_mask, kv_idx, o, lse,
                     workspace, workspace_bytes, stream);
+}
+
+hsv_status hsv_verify_attn_paged(const hsv_verify_desc *d, const void *q, const void *k_pool,
+                                 const void *v_pool, const int32_t *block_table,
+                                 int32_t n_pool_blocks, const int32_t *ctx_lens,
+                                 const int32_t *parent, const uint64_t *anc_mask, void *o,
+                                 float *lse, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (!d) return HSV_ERR_NULL;
+  if (d->block_size == 0) return HSV_ERR_SHAPE;
+  if (!block_table) return HSV_ERR_NULL;
+  return run_verify(d, false, q, k_pool, v_pool, ctx_lens, parent, anc_mask, nullptr, o, lse,
+                    workspace, workspace_bytes, stream, block_table, n_pool_blocks);
 }
 
 hsv_status hsv_tree_ancestor_mask(const int32_t *parent, uint64_t *anc_mask, int32_t batch,

@@ -37,6 +37,8 @@ struct Plan {
   const int32_t *parent;    // NULL when anc is given (or no tree part)
   const uint64_t *anc;      // NULL when parent is given
   const int32_t *kv_idx;    // sparse prefix, else NULL
+  const int32_t *block_table; // paged cache: [B][max_blocks] pool block of each
+                              // logical block of block_size rows; else NULL
   // outputs
   void *o;
   float *lse;
@@ -64,6 +66,9 @@ struct Plan {
   int32_t kgroups;          // partial results per slot workgroup
   int32_t n_parts;          // n_slots * kgroups
   int32_t row_chunks;       // workgroups per (slot, b, kv head) along rows
+  int32_t block_shift;      // paged: log2(block_size)
+  int32_t max_blocks;       // paged: cap / block_size (columns of block_table)
+  int32_t n_pool_blocks;    // paged: pool blocks in k and v
   float scale;              // score scale
   float scale_log2;         // scale * log2(e)
 };

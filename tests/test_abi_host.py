@@ -149,3 +149,37 @@ def test_product_package_does_not_reach_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text, f
                 assert "from oracle" not in text, f
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_size=64), 0), (dict(block_size=256), 0), (dict(block_size=16), 2),
+    (dict(block_size=96), 2), (dict(block_size=128, kv_capacity=32832), 2),
+    (dict(block_size=64, n_sel=100), 3),                         # sparse + paged
+    (dict(block_size=64, flags=2), 3),                           # no prefix
+    (dict(block_size=64, n_draft=16, n_q_heads=32), 3),          # 64 rows: MFMA kernel
+    (dict(block_size=64, head_dim=64), 3),                       # D 64
+    (dict(block_size=64, max_ctx=600000, kv_capacity=600064), 3),  # > 256 splits of 2048 keys
+])
+def test_paged_descriptors(hsv, kw, code):
+    if kw.get("block_size") and "kv_capacity" not in kw:
+        kw["kv_capacity"] = 32832 if 32832 % kw["block_size"] == 0 else 32768 + kw["block_size"]
+    got, n = _ws(hsv, _desc(hsv, **kw))
+    assert got == code
+    if code == 0:
+        assert n > 0
+
+
+def test_paged_call_argument_errors(hsv):
+    d = _desc(hsv, block_size=64)
+    n = _ws(hsv, d)[1]
+
+    def call(desc, table=FAKE, n_pool=10):
+        return hsv.lib.hsv_verify_attn_paged(ctypes.byref(desc), FAKE, FAKE, FAKE, table, n_pool,
+                                             FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                             ctypes.c_size_t(n), None)
+
+    assert call(d, table=None) == hsv.HSV_ERR_NULL
+    assert call(d, n_pool=0) == hsv.HSV_ERR_SHAPE
+    assert call(_desc(hsv)) == hsv.HSV_ERR_SHAPE                 # no block size
+    # a contiguous call must not carry a block size
+    assert _call_dense(hsv, d, ws_bytes=n) == hsv.HSV_ERR_SHAPE
