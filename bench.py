@@ -45,7 +45,8 @@ INFINITY_CACHE_BYTES = 256 * 2 ** 20
 # and the sources whose hash it records.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_partial_dma_tree32k_counters.md")
 KERNEL_SOURCES = ("long_context_tree_verify_amd/csrc/attn_dma.hip",
-                  "long_context_tree_verify_amd/csrc/common.hpp")
+                  "long_context_tree_verify_amd/csrc/common.hpp",
+                  "long_context_tree_verify_amd/csrc/plan.h")
 
 
 def log(msg):
@@ -104,6 +105,8 @@ def recorded_traffic(workload: str):
 def cpu_baseline(inp, target_s: float):
     """Time the fp64 oracle on a bounded sample of output rows and scale."""
     import numpy as np
+
+    import oracle
     wl = inp.wl
     B, N, Hq = wl.batch, wl.n_draft, wl.n_q_heads
     total = B * N * Hq
@@ -254,6 +257,77 @@ def measure_accept(hsv, dev, inp, steps: int):
                     "launch-bound at this size"}
 
 
+PAGED_BLOCK = 128
+
+
+def measure_paged(hsv, dev, inp, steps: int, out_dtype):
+    """The same verify step over a paged copy of the cache (pool blocks of
+    PAGED_BLOCK tokens in seeded random order, a block table), K steps in a
+    graph with the pool copies rotated like the contiguous measurement;
+    HIP events on the capture stream bracket the replay."""
+    import numpy as np
+    import torch
+
+    import synth
+    wl = inp.wl
+    bs = PAGED_BLOCK
+    S = inp.k.shape[2]
+    cap = -(-S // bs) * bs
+    pad = ((0, 0), (0, 0), (0, cap - S), (0, 0))
+    kp, vp, table = synth.to_paged(np.pad(inp.k, pad), np.pad(inp.v, pad), bs,
+                                   np.random.Generator(np.random.PCG64(7)))
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k0, v0 = up(kp), up(vp)
+    pool_bytes = 2 * k0.numel() * k0.element_size()
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / pool_bytes) + 1) if pool_bytes < \
+        2 * INFINITY_CACHE_BYTES else 1
+    ks, vs = [k0] + [k0.clone() for _ in range(copies - 1)], [v0] + [v0.clone()
+                                                                      for _ in range(copies - 1)]
+    q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    tab = torch.from_numpy(table).to(dev)
+    ctx = torch.from_numpy(inp.ctx_lens).to(dev)
+    parent = torch.from_numpy(inp.parent).to(dev)
+    B, N, Hq, D = q.shape
+    o = torch.empty((B, N, Hq, D), dtype=out_dtype, device=dev)
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    max_ctx = int(inp.ctx_lens.max())
+    desc = hsv.make_desc(batch=B, n_draft=N, n_q_heads=Hq, n_kv_heads=wl.n_kv_heads,
+                         head_dim=D, kv_capacity=cap, max_ctx=max_ctx, in_dtype=hsv.HSV_BF16,
+                         out_dtype=hsv.HSV_BF16 if out_dtype == torch.bfloat16 else hsv.HSV_F32,
+                         block_size=bs)
+    ws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+
+    def call(j):
+        hsv.hsv_verify_attn_paged(q, ks[j % copies], vs[j % copies], tab, ctx, parent,
+                                  max_ctx=max_ctx, out_dtype=out_dtype, o=o, lse=lse,
+                                  workspace=ws, stream=None)
+
+    for j in range(3):
+        call(j)
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for j in range(steps):
+            call(j)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = kv_bytes(inp)
+    return {"entry": "hsv_verify_attn_paged", "block_size": bs,
+            "workload": f"{wl.name}, pool blocks in random order, {copies} pool copies",
+            "us_per_step": round(us, 2), "kv_read_bytes": nbytes,
+            "achieved": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +337,8 @@ def main(argv=None) -> int:
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-cache measurement")
     ap.add_argument("--no-selection", action="store_true",
                     help="skip the index-set selection measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -433,6 +509,9 @@ def main(argv=None) -> int:
                    "graph_ms_per_step_events": round(graph_ms, 5),
                    "eager_ms_per_step": round(eager_ms, 5)},
     }
+    if inp.kv_idx is None and bf and wl.head_dim == 128 and not args.no_paged:
+        log("bench: timing the paged-cache step")
+        result["paged"] = measure_paged(hsv, dev, inp, args.steps, out_dtype)
     log("bench: timing the accepted-path cache update")
     result["accept"] = measure_accept(hsv, dev, inp, args.steps)
     if not args.no_selection:
