@@ -239,13 +239,23 @@ hsv_status hsv_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens,
  * c_b are not read); ctx_lens [B] int32 (device); kv_idx [B, Hkv, n_sel]
  * int32 out, strictly increasing -- if c_b < n_sel the tail is -1.
  * Requires n_sink + n_recent <= n_sel, n_draft_top >= 0 and
- * score_len <= 524288; the chosen set is unique (no randomness). */
+ * score_len <= 524288; the chosen set is unique (no randomness).
+ * `workspace` (device, 256-byte aligned, at least
+ * hsv_select_workspace_bytes) holds the candidate lists between the two
+ * launches; its contents on entry do not matter. */
 hsv_status hsv_select_kv_idx(const float *draft_score, const float *target_score,
-                             int32_t score_len, const int32_t *ctx_lens,
-                             int32_t batch, int32_t n_kv_heads, int32_t n_sel,
-                             int32_t n_sink, int32_t n_recent,
-                             int32_t n_draft_top, int32_t *kv_idx,
+                             int32_t score_len, const int32_t *ctx_lens, int32_t batch,
+                             int32_t n_kv_heads, int32_t n_sel, int32_t n_sink,
+                             int32_t n_recent, int32_t n_draft_top, int32_t *kv_idx,
+                             void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* Bytes of workspace hsv_select_kv_idx needs for these sizes (per (b, KV
+ * head) and 8192-position chunk of the score rows, two candidate lists of
+ * 1024 (key, position) slots and their counts).  HSV_ERR_SHAPE /
+ * HSV_ERR_UNSUPPORTED for sizes the call would reject. */
+hsv_status hsv_select_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t score_len,
+                                      size_t *bytes);
 
 /* Exact log-sum-exp merge of partial attention results (LongSpec section
  * 2.C: the parts' outputs are combined exactly), e.g. partials over disjoint

@@ -257,9 +257,17 @@ def hsv_lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype=torc
     return o, lse
 
 
+def hsv_select_workspace_bytes(batch: int, n_kv_heads: int, score_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.hsv_select_workspace_bytes(batch, n_kv_heads, score_len, ctypes.byref(n)),
+           "hsv_select_workspace_bytes")
+    return int(n.value)
+
+
 def hsv_select_kv_idx(draft_score: torch.Tensor, target_score: torch.Tensor,
                       ctx_lens: torch.Tensor, *, n_sel: int, n_sink: int, n_recent: int,
-                      n_draft_top: int, kv_idx=None, stream=None) -> torch.Tensor:
+                      n_draft_top: int, kv_idx=None, workspace=None, stream=None
+                      ) -> torch.Tensor:
     """Verification index set (see include/hsv.h): draft_score, target_score
     float32 [B, Hkv, L]; returns kv_idx int32 [B, Hkv, n_sel]."""
     if draft_score.dtype != torch.float32 or target_score.dtype != torch.float32 or \
@@ -272,9 +280,13 @@ def hsv_select_kv_idx(draft_score: torch.Tensor, target_score: torch.Tensor,
         kv_idx = torch.empty((B, Hkv, n_sel), dtype=torch.int32, device=draft_score.device)
     if kv_idx.dtype != torch.int32 or tuple(kv_idx.shape) != (B, Hkv, n_sel):
         raise ValueError("kv_idx must be int32 [B, Hkv, n_sel]")
-    _check_dev(draft_score, target_score, ctx_lens, kv_idx)
+    if workspace is None:
+        workspace = torch.empty(max(hsv_select_workspace_bytes(B, Hkv, L), 256),
+                                dtype=torch.uint8, device=draft_score.device)
+    _check_dev(draft_score, target_score, ctx_lens, kv_idx, workspace)
     _check(lib.hsv_select_kv_idx(_ptr(draft_score), _ptr(target_score), L, _ptr(ctx_lens), B, Hkv,
                                  n_sel, n_sink, n_recent, n_draft_top, _ptr(kv_idx),
+                                 _ptr(workspace), ctypes.c_size_t(workspace.numel()),
                                  _stream(stream, draft_score.device)), "hsv_select_kv_idx")
     return kv_idx
 

@@ -37,6 +37,7 @@ EXPORTS = (
     "hsv_gather_kv",
     "hsv_lse_merge",
     "hsv_select_kv_idx",
+    "hsv_select_workspace_bytes",
     "hsv_tree_position_ids",
     "hsv_accept_path",
     "hsv_status_string",
@@ -85,12 +86,14 @@ def load() -> ctypes.CDLL:
     lib.hsv_tree_ancestor_mask.argtypes = [P, P, i32, i32, P]
     lib.hsv_gather_kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     lib.hsv_lse_merge.argtypes = [P, P, i32, i64, i32, P, P, i32, P]
-    lib.hsv_select_kv_idx.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, i32, P, P]
+    lib.hsv_select_kv_idx.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, i32, P, P, sz, P]
+    lib.hsv_select_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
     lib.hsv_tree_position_ids.argtypes = [P, P, P, i32, i32, P]
     lib.hsv_accept_path.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     for name in ("hsv_verify_workspace_bytes", "hsv_verify_attn", "hsv_verify_attn_sparse",
                  "hsv_verify_attn_paged", "hsv_tree_ancestor_mask", "hsv_gather_kv", "hsv_lse_merge",
-                 "hsv_select_kv_idx", "hsv_tree_position_ids", "hsv_accept_path"):
+                 "hsv_select_kv_idx", "hsv_select_workspace_bytes", "hsv_tree_position_ids",
+                 "hsv_accept_path"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hsv_status_string.argtypes = [ctypes.c_int]
     lib.hsv_status_string.restype = ctypes.c_char_p

@@ -351,19 +351,35 @@ hsv_status hsv_gather_kv(const void *k_cache, const void *v_cache, const int32_t
              : HSV_ERR_HIP;
 }
 
+hsv_status hsv_select_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t score_len,
+                                      size_t *bytes) {
+  if (!bytes) return HSV_ERR_NULL;
+  if (batch < 1 || n_kv_heads < 1 || score_len < 1) return HSV_ERR_SHAPE;
+  if (score_len > select_max_positions()) return HSV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(batch) * n_kv_heads > (int64_t{1} << 24)) return HSV_ERR_SHAPE;
+  *bytes = select_workspace_bytes(batch, n_kv_heads, score_len);
+  return HSV_OK;
+}
+
 hsv_status hsv_select_kv_idx(const float *draft_score, const float *target_score,
                              int32_t score_len, const int32_t *ctx_lens, int32_t batch,
                              int32_t n_kv_heads, int32_t n_sel, int32_t n_sink, int32_t n_recent,
-                             int32_t n_draft_top, int32_t *kv_idx, hipStream_t stream) {
+                             int32_t n_draft_top, int32_t *kv_idx, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   if (!draft_score || !target_score || !ctx_lens || !kv_idx) return HSV_ERR_NULL;
-  if (batch < 1 || n_kv_heads < 1 || n_sel < 1 || score_len < 1) return HSV_ERR_SHAPE;
+  size_t need = 0;
+  const hsv_status st = hsv_select_workspace_bytes(batch, n_kv_heads, score_len, &need);
+  if (st != HSV_OK) return st;
+  if (n_sel < 1) return HSV_ERR_SHAPE;
   if (n_sink < 0 || n_recent < 0 || n_draft_top < 0 ||
       static_cast<int64_t>(n_sink) + n_recent > n_sel)
     return HSV_ERR_SHAPE;
-  if (score_len > select_max_positions()) return HSV_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(batch) * n_kv_heads > (int64_t{1} << 31) - 1) return HSV_ERR_SHAPE;
+  if (!workspace) return HSV_ERR_WORKSPACE;
+  if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return HSV_ERR_WORKSPACE;
   return launch_select_kv_idx(draft_score, target_score, score_len, ctx_lens, batch, n_kv_heads,
-                              n_sel, n_sink, n_recent, n_draft_top, kv_idx, stream) == hipSuccess
+                              n_sel, n_sink, n_recent, n_draft_top, kv_idx, workspace,
+                              stream) == hipSuccess
              ? HSV_OK
              : HSV_ERR_HIP;
 }

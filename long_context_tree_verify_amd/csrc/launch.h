@@ -49,8 +49,9 @@ hipError_t launch_gather_kv(const void *k, const void *v, const int32_t *idx, vo
 hipError_t launch_select_kv_idx(const float *draft, const float *target, int score_len,
                                 const int32_t *ctx_lens, int batch, int hkv, int n_sel,
                                 int n_sink, int n_recent, int n_draft_top, int32_t *kv_idx,
-                                hipStream_t s);
+                                void *workspace, hipStream_t s);
 int select_max_positions();
+size_t select_workspace_bytes(int batch, int hkv, int score_len);
 // Tree position ids and the accepted-path cache update.
 hipError_t launch_tree_position_ids(const int32_t *parent, const int32_t *ctx_lens,
                                     int32_t *pos_ids, int batch, int n_draft, hipStream_t s);

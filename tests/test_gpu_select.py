@@ -121,23 +121,47 @@ def test_rejects_bad_arguments(hsv, gpu):
         hsv.hsv_select_kv_idx(big, big, c, n_sel=4, n_sink=0, n_recent=0, n_draft_top=0)
 
 
-def test_sample_defeating_map(hsv, gpu):
-    # Rows of 65536 keep 64 keys per thread (position j * 1024 + t) and
-    # sample column j of thread t when j % 16 == (t // 64) % 16.  Here 500
-    # sampled positions hold the only large scores: the floor taken from the
-    # sample leaves fewer than k keys, so the selection must fall back to
-    # every candidate.  A second row puts the large scores off the sample.
-    L = 65536
+def _sample_positions(lo, hi):
+    # the filter's sample of the candidates [lo, hi): all of them up to 2048,
+    # else 32 segments of 64 consecutive positions spread evenly
+    n = hi - lo
+    if n <= 2048:
+        return np.arange(lo, hi)
+    starts = lo + ((n - 64) * np.arange(32)) // 31
+    return (starts[:, None] + np.arange(64)[None]).reshape(-1)
+
+
+def test_sample_defeating_maps(hsv, gpu):
+    # Row 0: the only large scores sit on 500 sampled positions, so the floor
+    # leaves fewer than k candidates: both maps must fall back to the
+    # streaming select.  Row 1: 3000 large scores off the sample, packed
+    # into one 8192-position chunk: its list overflows, again a fallback.
+    # Row 2: no planted values (the list path).
+    L, n_sink, n_recent = 65536, 4, 512
     rng = np.random.Generator(np.random.PCG64(511))
-    p = np.arange(L)
-    sampled = np.flatnonzero((p // 1024) % 16 == (p % 1024 // 64) % 16)
-    unsampled = np.setdiff1d(p, sampled)
-    draft = rng.random((2, 1, L), dtype=np.float32)
-    target = rng.random((2, 1, L), dtype=np.float32)
-    for row, pool in ((0, sampled), (1, unsampled)):
-        hot = rng.choice(pool[(pool >= 4) & (pool < L - 512)], 500, replace=False)
+    lo, hi = n_sink, L - n_recent
+    sampled = _sample_positions(lo, hi)
+    off = np.setdiff1d(np.arange(lo, hi), sampled)
+    draft = rng.random((3, 1, L), dtype=np.float32)
+    target = rng.random((3, 1, L), dtype=np.float32)
+    hot0 = rng.choice(sampled, 500, replace=False)
+    in_chunk = off[(off >= 16384) & (off < 24576)]
+    hot1 = rng.choice(in_chunk, 3000, replace=False)
+    for row, hot in ((0, hot0), (1, hot1)):
         draft[row, 0, hot] += 1000.0
         target[row, 0, hot] += 1000.0
-    ctx = np.array([L, L], np.int32)
-    _check(hsv, gpu, draft, target, ctx, "sample-defeating", n_sel=4096, n_sink=4,
-           n_recent=512, n_draft_top=1790)
+    ctx = np.full(3, L, np.int32)
+    _check(hsv, gpu, draft, target, ctx, "sample-defeating", n_sel=4096, n_sink=n_sink,
+           n_recent=n_recent, n_draft_top=1790)
+
+
+def test_tiny_rows(hsv, gpu):
+    # rows with fewer than 4 candidates take the single-load staging path
+    rng = np.random.Generator(np.random.PCG64(512))
+    ctx = np.array([3, 2, 1, 7], np.int32)
+    draft = rng.random((4, 2, 7), dtype=np.float32)
+    target = rng.random((4, 2, 7), dtype=np.float32)
+    _check(hsv, gpu, draft, target, ctx, "tiny rows", n_sel=2, n_sink=0, n_recent=0,
+           n_draft_top=1)
+    _check(hsv, gpu, draft, target, ctx, "tiny rows, window", n_sel=3, n_sink=0, n_recent=1,
+           n_draft_top=1)
