@@ -78,6 +78,20 @@ __device__ __forceinline__ Budget budget(int ctx, int score_len, int n_sel, int 
   return bd;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2,
+// 4 and 8 scan each 16-lane row, then row broadcasts of lanes 15 and 31 carry
+// the row totals forward (lanes a DPP move does not write read 0).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  int v = static_cast<int>(x);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return static_cast<uint32_t>(v);
+}
+
 // Exclusive prefix sum of `x` over a workgroup of NT threads, in thread
 // order; `total` receives the sum.  Uses `scratch` (NT / 64 words).
 template <int NT>
@@ -85,12 +99,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *s
                                                          uint32_t *total) {
   constexpr int kW = NT / kWave;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  uint32_t incl = x;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_inclusive_scan(x);
   if (lane == kWave - 1) scratch[wave] = incl;
   __syncthreads();
   uint32_t wave_base = 0, all = 0;
@@ -111,8 +120,10 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *s
 // descending bin order.  The one thread whose bin holds it writes *digit,
 // *need_out (the rank inside the bin) and *in_bin (the bin's count); the
 // caller then meets at a barrier.  The histogram must hold at least `need`.
+// Each thread zeroes the bins it read, so after that barrier the histogram
+// is clear for the next pass.
 template <int NT, int COPIES>
-__device__ __forceinline__ void find_digit(const uint32_t *hist, uint32_t need, uint32_t *scan,
+__device__ __forceinline__ void find_digit(uint32_t *hist, uint32_t need, uint32_t *scan,
                                            uint32_t *digit, uint32_t *need_out,
                                            uint32_t *in_bin) {
   constexpr int kPer = kBins / NT;
@@ -123,7 +134,10 @@ __device__ __forceinline__ void find_digit(const uint32_t *hist, uint32_t need, 
   for (int i = 0; i < kPer; ++i) {
     uint32_t s = 0;
 #pragma unroll
-    for (int cp = 0; cp < COPIES; ++cp) s += hist[(top - i) * COPIES + cp];
+    for (int cp = 0; cp < COPIES; ++cp) {
+      s += hist[(top - i) * COPIES + cp];
+      hist[(top - i) * COPIES + cp] = 0u;
+    }
     cnt[i] = s;
     mine += s;
   }
@@ -249,11 +263,11 @@ __device__ uint32_t sample_floor(const float *row, int lo, int n_cand, int k, Fi
 #pragma unroll
   for (int u = 0; u < kPer; ++u) key[u] = tid + kFiltThreads * u < n_smp ? order_key(v[u]) : 0u;
   uint32_t prefix = 0, pmask = 0, need = r;
+  for (int i = tid; i < kBins; i += kFiltThreads) sh.hist[i] = 0u;
+  __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 21 : 10;
-    for (int i = tid; i < kBins; i += kFiltThreads) sh.hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if (key[u] != 0u && (key[u] & pmask) == prefix)
@@ -264,8 +278,8 @@ __device__ uint32_t sample_floor(const float *row, int lo, int n_cand, int k, Fi
     prefix |= sh.digit << shift;
     pmask |= static_cast<uint32_t>(kBins - 1) << shift;
     need = sh.need;
-    __syncthreads();
   }
+  __syncthreads();  // sh.digit / sh.need are read before anyone rewrites them
   return max(prefix, 1u);
 }
 
@@ -436,13 +450,13 @@ __device__ bool list_select(const uint32_t *counts, const uint2 *lists, int bg, 
   constexpr uint32_t kPosMask = (1u << kPosBits) - 1;
   const uint32_t copy = static_cast<uint32_t>(lane) & 1u;
   uint32_t kpre = 0, kmask = 0, ppre = 0, pmask = 0, need = k, in_bin = 0;
+  for (int i = tid; i < kBins * 2; i += kSelThreads) sh.hist2[i] = 0u;
+  __syncthreads();
   for (int pass = 0; pass < 5; ++pass) {
     if (pass == 3 && need == in_bin) break;  // every key equal to the k-th is taken
     const bool on_pos = pass >= 3;
     const int shift = pass == 0 ? 21 : pass == 1 ? 10 : pass == 3 ? 8 : 0;
     const uint32_t dmask = pass == 2 ? 1023u : pass == 4 ? 255u : 2047u;
-    for (int i = tid; i < kBins * 2; i += kSelThreads) sh.hist2[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kMaxListChunks; ++u) {
       const uint32_t inv = kPosMask - e[u].y;
@@ -463,8 +477,8 @@ __device__ bool list_select(const uint32_t *counts, const uint2 *lists, int bg, 
     }
     need = sh.need;
     in_bin = sh.in_bin;
-    __syncthreads();
   }
+  __syncthreads();  // sh.digit / sh.need are read before anyone rewrites them
   // mark every value at or above the k-th: key above it, or equal key and
   // (when positions were resolved) position at or before it
 #pragma unroll
