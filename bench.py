@@ -330,6 +330,59 @@ def measure_paged(hsv, dev, inp, steps: int, out_dtype):
             "achieved": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s"}
 
 
+def measure_recall(hsv, dev, steps: int):
+    """Attention recall rate of the selected index sets (Dustin page,
+    methodology 2 names the rate; reading: the share of the full prefix's
+    softmax mass the set keeps, exp(lse_set - lse_full) per query row) on
+    the workload with 256 planted heavy-hitter keys per (sequence, KV head):
+    importance maps that flag most of those keys -> hsv_select_kv_idx ->
+    prefix-only sparse attention over the set, against prefix-only dense
+    attention.  A random Zipf-ranked set of the same size is the contrast.
+    Also times the selection on these maps."""
+    import numpy as np
+    import torch
+
+    import synth
+    sh = SELECT_SHAPE
+    log("bench: generating the heavy-hitter workload for the recall rate")
+    inp = synth.make_inputs("sparse64k_hh")
+    wl = inp.wl
+    B, H, L = wl.batch, wl.n_kv_heads, inp.k.shape[2]
+    rng = np.random.Generator(np.random.PCG64(sh["seed"]))
+    draft_np, target_np = synth.heavy_importance_maps(rng, inp, L)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    ctx = torch.from_numpy(inp.ctx_lens).to(dev)
+    parent = torch.from_numpy(inp.parent).to(dev)
+    draft, target = torch.from_numpy(draft_np).to(dev), torch.from_numpy(target_np).to(dev)
+    kv_idx = torch.empty((B, H, wl.n_sel), dtype=torch.int32, device=dev)
+    ws = torch.empty(hsv.hsv_select_workspace_bytes(B, H, L), dtype=torch.uint8, device=dev)
+    kw = dict(n_sel=wl.n_sel, n_sink=wl.n_sink, n_recent=wl.n_recent,
+              n_draft_top=sh["n_draft_top"], kv_idx=kv_idx, workspace=ws)
+    hsv.hsv_select_kv_idx(draft, target, ctx, **kw)
+    max_ctx = int(inp.ctx_lens.max())
+    flags = hsv.HSV_FLAG_NO_TREE
+    _, lse_full = hsv.hsv_verify_attn(q, k, v, ctx, parent, max_ctx=max_ctx, flags=flags)
+    _, lse_sel = hsv.hsv_verify_attn_sparse(q, k, v, ctx, parent, None, kv_idx,
+                                            max_ctx=max_ctx, flags=flags)
+    rand_idx = torch.from_numpy(inp.kv_idx).to(dev)
+    _, lse_rand = hsv.hsv_verify_attn_sparse(q, k, v, ctx, parent, None, rand_idx,
+                                             max_ctx=max_ctx, flags=flags)
+    torch.cuda.synchronize()
+    arr = torch.exp(lse_sel.double() - lse_full.double())
+    arr_rand = torch.exp(lse_rand.double() - lse_full.double())
+    return {"workload": f"{wl.name}: {wl.description}",
+            "set": f"{wl.n_sel} positions (sinks {wl.n_sink}, window {wl.n_recent}, draft top "
+                   f"{sh['n_draft_top']}) from maps flagging 70 % (draft) / 80 % (target) "
+                   f"of the planted keys",
+            "arr_mean": round(float(arr.mean()), 4), "arr_min": round(float(arr.min()), 4),
+            "arr_random_set_mean": round(float(arr_rand.mean()), 4),
+            "rows": int(arr.numel())}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -519,6 +572,7 @@ def main(argv=None) -> int:
     if not args.no_selection:
         log("bench: timing the index-set selection")
         result["selection"] = measure_selection(hsv, dev, args.steps, args.warmup)
+        result["selection"]["recall"] = measure_recall(hsv, dev, args.steps)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

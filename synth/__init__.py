@@ -20,6 +20,7 @@ from .gen import (  # noqa: F401
     block_masks,
     random_masks,
     f32_to_bf16_bits,
+    heavy_importance_maps,
     importance_maps,
     make_inputs,
     random_tree_parents,

@@ -247,6 +247,8 @@ class Workload:
     n_sink: int = 4
     n_recent: int = 512
     zipf_a: float = 1.1
+    n_heavy: int = 0              # > 0: keys planted per (b, kv head) that draw most attention
+    heavy_logit: float = 6.0      # their score against the head's mean query direction
     description: str = ""
 
     @property
@@ -291,6 +293,12 @@ WORKLOADS: Dict[str, Workload] = {
         n_draft=8, ctx=(65536, 65536), dtype="bf16", tree="chain",
         q_scale=0.5, kv_scale=0.5, n_sel=4096, n_sink=4, n_recent=512, zipf_a=1.1,
         description="batch 8, 32/8 heads, D128, bf16, 65536-token context, 4096-entry index sets"),
+    "sparse64k_hh": Workload(
+        name="sparse64k_hh", seed=6, batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        n_draft=8, ctx=(65536, 65536), dtype="bf16", tree="chain",
+        q_scale=0.5, kv_scale=0.5, n_sel=4096, n_sink=4, n_recent=512, zipf_a=1.1,
+        n_heavy=256, heavy_logit=8.0,
+        description="sparse64k with 256 planted heavy-hitter keys per (sequence, KV head)"),
 }
 
 
@@ -304,6 +312,7 @@ class VerifyInputs:
     parent: np.ndarray             # int32 [B, N]
     kv_idx: Optional[np.ndarray] = None   # int32 [B, Hkv, n_sel]
     meta: Dict[str, str] = field(default_factory=dict)
+    heavy: Optional[np.ndarray] = None    # int32 [B, Hkv, n_heavy] planted positions
 
     @property
     def is_bf16(self) -> bool:
@@ -401,5 +410,50 @@ def make_inputs(wl, seed: Optional[int] = None, poison_unselected: bool = False,
             cache[b] = _encode(x, wl.dtype)
         caches.append(cache)
     k, v = caches
-    return VerifyInputs(wl=wl, q=q, k=k, v=v, ctx_lens=ctx, parent=parent, kv_idx=kv_idx,
-                        meta={"seed": str(seed), "workload": wl.name})
+
+    # 7. planted heavy hitters: each (b, g) gets a random unit direction u;
+    # its queries gain u (unit length) and n_heavy of its prefix positions
+    # (not sinks, not the recent window) gain heavy_logit * sqrt(D) * u, so
+    # those keys score about heavy_logit against every query of the group and
+    # draw most of the softmax mass
+    heavy = None
+    if wl.n_heavy:
+        heavy = np.empty((B, Hkv, wl.n_heavy), dtype=np.int32)
+        G = Hq // Hkv
+        qf = bf16_bits_to_f32(q) if wl.dtype == "bf16" else q.copy()
+        for b in range(B):
+            c = int(ctx[b])
+            lo, hi = min(wl.n_sink, c), max(c - wl.n_recent, min(wl.n_sink, c))
+            for g in range(Hkv):
+                pos = np.sort(rng.choice(np.arange(lo, hi), wl.n_heavy, replace=False))
+                heavy[b, g] = pos
+                u = rng.standard_normal(D)
+                u = (u / np.linalg.norm(u)).astype(np.float32)
+                qf[b, :, g * G:(g + 1) * G, :] += u
+                kf = bf16_bits_to_f32(k[b, g, pos]) if wl.dtype == "bf16" else k[b, g, pos]
+                kf = kf + np.float32(wl.heavy_logit * np.sqrt(D)) * u[None]
+                k[b, g, pos] = _encode(kf.astype(np.float32), wl.dtype)
+        q = _encode(qf, wl.dtype)
+    out = VerifyInputs(wl=wl, q=q, k=k, v=v, ctx_lens=ctx, parent=parent, kv_idx=kv_idx,
+                       meta={"seed": str(seed), "workload": wl.name})
+    out.heavy = heavy
+    return out
+
+
+def heavy_importance_maps(rng: np.random.Generator, inp: "VerifyInputs", score_len: int,
+                          recall_target: float = 0.8, recall_draft: float = 0.7,
+                          lift: float = 50.0):
+    """Importance maps for a workload with planted heavy hitters: the
+    background of `importance_maps`, with a `recall_target` share (target
+    map) and a separately drawn `recall_draft` share (draft map) of each
+    (b, g)'s heavy positions raised `lift` times -- signals that point at
+    most, not all, of the keys that matter.  Returns (draft, target)."""
+    draft, target = importance_maps(rng, inp.ctx_lens, inp.wl.n_kv_heads, score_len)
+    B, H = inp.heavy.shape[:2]
+    for b in range(B):
+        for g in range(H):
+            pos = inp.heavy[b, g]
+            for m, share in ((target, recall_target), (draft, recall_draft)):
+                pick = pos[rng.random(pos.size) < share]
+                m[b, g, pick] = (m[b, g, pick] * lift).astype(np.float32)
+    return draft, target

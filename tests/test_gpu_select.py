@@ -165,3 +165,49 @@ def test_tiny_rows(hsv, gpu):
            n_draft_top=1)
     _check(hsv, gpu, draft, target, ctx, "tiny rows, window", n_sel=3, n_sink=0, n_recent=1,
            n_draft_top=1)
+
+
+def test_recall_rate_parity(hsv, gpu):
+    # Attention recall rate of a selected set, exp(lse_set - lse_full) over
+    # the prefix, from the GPU's LSEs against the oracle's.  Bound: each LSE
+    # is within 1e-3 * max(|lse|, 1) of the oracle's, so the rate is within
+    # a factor exp(+-2e-3 * max|lse|) of the oracle's rate.  On a workload
+    # with planted heavy-hitter keys the selected set must also keep more
+    # mass than the random set of the same size.
+    import torch
+    inp = synth.make_inputs("sparse64k_hh", batch=2, n_kv_heads=2, n_q_heads=8,
+                            ctx=(8192, 8192), n_heavy=64, n_sel=1024, n_recent=128)
+    L = inp.k.shape[2]
+    rng = np.random.Generator(np.random.PCG64(513))
+    draft, target = synth.heavy_importance_maps(rng, inp, L)
+    kw = dict(n_sel=1024, n_sink=4, n_recent=128, n_draft_top=400)
+    ctx = inp.ctx_lens
+    kv = _select(hsv, gpu, draft, target, ctx, **kw)
+    np.testing.assert_array_equal(kv, oracle.select_kv_idx(draft, target, ctx, **kw))
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(gpu)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    c = torch.from_numpy(ctx).to(gpu)
+    flags = hsv.HSV_FLAG_NO_TREE
+    _, l_full = hsv.hsv_verify_attn(q, k, v, c, None, max_ctx=int(ctx.max()), flags=flags)
+    _, l_sel = hsv.hsv_verify_attn_sparse(q, k, v, c, None, None, torch.from_numpy(kv).to(gpu),
+                                          max_ctx=int(ctx.max()), flags=flags)
+    _, l_rand = hsv.hsv_verify_attn_sparse(q, k, v, c, None, None,
+                                           torch.from_numpy(inp.kv_idx).to(gpu),
+                                           max_ctx=int(ctx.max()), flags=flags)
+    torch.cuda.synchronize()
+    l_full, l_sel, l_rand = (x.cpu().numpy().astype(np.float64) for x in (l_full, l_sel, l_rand))
+    _, r_full = oracle.verify_attn(inp.q, inp.k, inp.v, ctx, parent=inp.parent, bf16=True,
+                                   parts=oracle.PART_PREFIX)
+    _, r_sel = oracle.verify_attn(inp.q, inp.k, inp.v, ctx, parent=inp.parent, kv_idx=kv,
+                                  bf16=True, parts=oracle.PART_PREFIX)
+    arr_gpu = np.exp(l_sel - l_full)
+    arr_ref = oracle.recall_rate(r_sel, r_full)
+    bound = np.exp(2e-3 * np.maximum(np.abs(r_full), 1.0)) - 1.0
+    rel = np.abs(arr_gpu / arr_ref - 1.0)
+    log(f"  recall rate: mean {arr_gpu.mean():.4f} (oracle {arr_ref.mean():.4f}), "
+        f"max rel diff {rel.max():.2e}, random set {np.exp(l_rand - l_full).mean():.4f}")
+    assert (rel <= bound).all()
+    assert arr_gpu.mean() > 2.0 * np.exp(l_rand - l_full).mean()
