@@ -88,17 +88,24 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
+def mask_words(n: int) -> int:
+    """64-bit words of one node's mask: word w holds nodes 64w .. 64w + 63."""
+    return (n + 63) // 64
+
+
 def ancestor_mask(parent: np.ndarray) -> np.ndarray:
-    """uint64 [B, N] ancestor bitmask by walking parent pointers."""
+    """Ancestor-or-self bitmask by walking parent pointers: uint64 [B, N] for
+    N <= 64, else [B, N, W] with W = ceil(N / 64) words per node."""
     parent = np.ascontiguousarray(parent, dtype=np.int32)
     if parent.ndim == 1:
         parent = parent[None]
     B, N = parent.shape
-    out = np.zeros((B, N), dtype=np.uint64)
+    W = mask_words(N)
+    out = np.zeros((B, N, W), dtype=np.uint64)
     rc = _load().oracle_ancestor_mask(_ptr(parent), B, N, _ptr(out))
     if rc != 0:
         raise ValueError("invalid parent array")
-    return out
+    return out.reshape(B, N) if W == 1 else out
 
 
 def verify_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_lens: np.ndarray,
@@ -127,7 +134,7 @@ def verify_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_lens: np.ndarra
     if parent is not None:
         parent = np.ascontiguousarray(parent, dtype=np.int32).reshape(B, N)
     if anc_mask is not None:
-        anc_mask = np.ascontiguousarray(anc_mask, dtype=np.uint64).reshape(B, N)
+        anc_mask = np.ascontiguousarray(anc_mask, dtype=np.uint64).reshape(B, N, mask_words(N))
     n_sel = 0
     if kv_idx is not None:
         kv_idx = np.ascontiguousarray(kv_idx, dtype=np.int32)

@@ -31,21 +31,23 @@ int oracle_ancestor_mask(const int32_t *parent, int32_t batch, int32_t n_draft,
                          uint64_t *anc) {
   /* LongSpec page, section 1 (tree attention) and 2.C (masks specific to the
    * branches of the speculation tree): node i sees itself and the nodes on its
-   * path to the prefix root.  Walk the path one parent at a time. */
-  if (n_draft < 0 || n_draft > 64) return -1;
+   * path to the prefix root.  Walk the path one parent at a time.  A node's
+   * mask takes W = ceil(N / 64) words; word w holds nodes 64w .. 64w + 63. */
+  if (n_draft < 0 || n_draft > ORACLE_MAX_DRAFT) return -1;
+  const int32_t W = (n_draft + 63) / 64;
   for (int32_t b = 0; b < batch; ++b) {
     for (int32_t i = 0; i < n_draft; ++i) {
       int32_t p = parent[(int64_t)b * n_draft + i];
       if (p < -1 || p >= i) return -1;
     }
     for (int32_t i = 0; i < n_draft; ++i) {
-      uint64_t bits = 0;
+      uint64_t *row = anc + ((int64_t)b * n_draft + i) * W;
+      for (int32_t w = 0; w < W; ++w) row[w] = 0;
       int32_t j = i;
       while (j >= 0) {
-        bits |= (uint64_t)1 << j;
+        row[j / 64] |= (uint64_t)1 << (j % 64);
         j = parent[(int64_t)b * n_draft + j];
       }
-      anc[(int64_t)b * n_draft + i] = bits;
     }
   }
   return 0;
@@ -100,9 +102,10 @@ static void attend_row(const oracle_desc *d, const void *q, const void *k,
   }
   if (d->parts & ORACLE_PART_TREE) {
     if (anc_mask) {
-      uint64_t bits = anc_mask[(int64_t)b * N + i];
+      const int32_t W = (N + 63) / 64;
+      const uint64_t *row = anc_mask + ((int64_t)b * N + i) * W;
       for (int32_t j = 0; j < N; ++j)
-        if ((bits >> j) & 1u) mask[c + j] = 1;
+        if ((row[j / 64] >> (j % 64)) & 1u) mask[c + j] = 1;
     } else {
       int32_t j = i;
       while (j >= 0) {
@@ -153,7 +156,7 @@ int oracle_verify_attn(const oracle_desc *d, const void *q, const void *k,
                        int64_t n_rows, double *o, double *lse) {
   if (!d || !q || !k || !v || !ctx_lens || !o || !lse) return -1;
   if ((parent == NULL) == (anc_mask == NULL)) return -1;
-  if (d->n_draft < 1 || d->n_draft > 64 || d->head_dim < 1) return -1;
+  if (d->n_draft < 1 || d->n_draft > ORACLE_MAX_DRAFT || d->head_dim < 1) return -1;
   if (d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads) return -1;
   if (d->n_sel > 0 && !kv_idx) return -1;
   for (int32_t b = 0; b < d->batch; ++b) {

@@ -17,7 +17,7 @@
  *       P(b,g) = [0, c_b)                 dense
  *              = { kv_idx[b,g,k] }        sparse
  *       T(b,i) = { i, parent[i], parent[parent[i]], ... }   (walk until -1)
- *                or the set bits of anc_mask[b,i] when given instead
+ *                or the set bits of anc_mask[b,i,:] when given instead
  *     s_t = scale * sum_d q[b,i,h,d] * k[b,g,t,d]          (fp64)
  *     lse = log sum_{t in A} exp(s_t)                      (max-shifted)
  *     o   = sum_{t in A} exp(s_t - lse) * v[b,g,t,:]
@@ -34,6 +34,7 @@ extern "C" {
 
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
 enum { ORACLE_PART_PREFIX = 1, ORACLE_PART_TREE = 2 };
+enum { ORACLE_MAX_DRAFT = 256 }; /* draft nodes per sequence */
 
 typedef struct {
   int32_t batch, n_draft, n_q_heads, n_kv_heads, head_dim;
@@ -45,7 +46,8 @@ typedef struct {
 } oracle_desc;
 
 /* Ancestor sets by walking parent pointers one by one.
- * parent: [B, N], parent[i] in [-1, i-1].  anc: [B, N]; bit j set iff node j
+ * parent: [B, N], parent[i] in [-1, i-1], N <= ORACLE_MAX_DRAFT.
+ * anc: [B, N, W], W = ceil(N / 64); bit j % 64 of word j / 64 set iff node j
  * is node i or one of its ancestors.  Returns 0, or -1 for a parent out of
  * range (anc left unspecified). */
 int oracle_ancestor_mask(const int32_t *parent, int32_t batch, int32_t n_draft,
@@ -53,7 +55,7 @@ int oracle_ancestor_mask(const int32_t *parent, int32_t batch, int32_t n_draft,
 
 /* Verification attention for a list of rows.
  * q: [B, N, Hq, D]; k, v: [B, Hkv, S_cap, D]; ctx_lens: [B];
- * exactly one of parent [B, N] / anc_mask [B, N] non-NULL;
+ * exactly one of parent [B, N] / anc_mask [B, N, ceil(N/64)] non-NULL;
  * kv_idx: [B, Hkv, n_sel] when n_sel > 0, else ignored.
  * rows: n_rows (b, i, h) triples, or NULL for every row (n_rows ignored).
  * o: [n_rows, D] (or [B, N, Hq, D] when rows is NULL), lse: [n_rows].
