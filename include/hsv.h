@@ -44,7 +44,9 @@
  *   k, v     [B, Hkv, S_cap, D]  in_dtype
  *   ctx_lens [B]                 int32
  *   parent   [B, N]              int32
- *   anc_mask [B, N]              uint64, bit j = node j visible from node i
+ *   anc_mask [B, N, W]           uint64, W = ceil(N / 64) words per node;
+ *                                bit j % 64 of word j / 64 = node j visible
+ *                                from node i ([B, N] when N <= 64)
  *   kv_idx   [B, Hkv, n_sel]     int32, strictly increasing, each < c_b
  *   o        [B, N, Hq, D]       out_dtype
  *   lse      [B, N, Hq]          float
@@ -99,7 +101,9 @@ typedef enum hsv_dtype { HSV_F32 = 0, HSV_BF16 = 1 } hsv_dtype;
 
 typedef struct hsv_verify_desc {
   int32_t batch;       /* B >= 1                                                */
-  int32_t n_draft;     /* N in [1, 64]                                          */
+  int32_t n_draft;     /* N in [1, 256]; above 64 only where the call uses the  */
+                       /* 256-row kernel (bf16, D = 128, more than 128        */
+                       /* grouped rows), else HSV_ERR_UNSUPPORTED             */
   int32_t n_q_heads;   /* Hq >= 1, a multiple of n_kv_heads                     */
   int32_t n_kv_heads;  /* Hkv >= 1                                              */
   int32_t head_dim;    /* D: 64 or 128                                          */
@@ -178,9 +182,10 @@ hsv_status hsv_verify_attn_paged(const hsv_verify_desc *d, const void *q,
 
 /* Ancestor bitmask of each draft tree (LongSpec section 2.C: the mask of the
  * speculative part follows the branches of the tree).
- * parent [B, N] int32 in [-1, i-1]; anc_mask [B, N] uint64 out, bit j set iff
- * node j is node i or an ancestor of i.  N in [1, 64].  Entries of a
- * sequence with an out-of-range parent are written as 0. */
+ * parent [B, N] int32 in [-1, i-1]; anc_mask [B, N, W] uint64 out
+ * (W = ceil(N / 64)), bit j % 64 of word j / 64 set iff node j is node i or
+ * an ancestor of i.  N in [1, 256].  Entries of a sequence with an
+ * out-of-range parent are written as 0. */
 hsv_status hsv_tree_ancestor_mask(const int32_t *parent, uint64_t *anc_mask,
                                   int32_t batch, int32_t n_draft,
                                   hipStream_t stream);

@@ -59,6 +59,18 @@ def _check_dev(*ts):
                 raise ValueError("tensors must be contiguous")
 
 
+def mask_words(n: int) -> int:
+    """64-bit words of one draft node's mask (word w: nodes 64w .. 64w+63)."""
+    return (n + 63) // 64
+
+
+def _check_mask(anc_mask, B, N):
+    shapes = {(B, N)} if N <= 64 else {(B, N, mask_words(N))}
+    if anc_mask is not None and (anc_mask.dtype not in (torch.int64, torch.uint64)
+                                 or tuple(anc_mask.shape) not in shapes):
+        raise ValueError("anc_mask must be 64-bit [B, N] (N <= 64) or [B, N, ceil(N/64)]")
+
+
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -98,9 +110,7 @@ def _verify(sparse: bool, q, k_cache, v_cache, ctx_lens, parent, anc_mask, kv_id
         raise ValueError("ctx_lens must be int32 [B]")
     if parent is not None and (parent.dtype != torch.int32 or tuple(parent.shape) != (B, N)):
         raise ValueError("parent must be int32 [B, N]")
-    if anc_mask is not None and (anc_mask.dtype not in (torch.int64, torch.uint64)
-                                 or tuple(anc_mask.shape) != (B, N)):
-        raise ValueError("anc_mask must be 64-bit [B, N]")
+    _check_mask(anc_mask, B, N)
     n_sel = 0
     if sparse:
         if kv_idx is None or kv_idx.dtype != torch.int32 or kv_idx.dim() != 3 or \
@@ -180,9 +190,7 @@ def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
         raise ValueError("ctx_lens must be int32 [B]")
     if parent is not None and (parent.dtype != torch.int32 or tuple(parent.shape) != (B, N)):
         raise ValueError("parent must be int32 [B, N]")
-    if anc_mask is not None and (anc_mask.dtype not in (torch.int64, torch.uint64)
-                                 or tuple(anc_mask.shape) != (B, N)):
-        raise ValueError("anc_mask must be 64-bit [B, N]")
+    _check_mask(anc_mask, B, N)
     if o is None:
         o = torch.empty((B, N, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None:
@@ -209,12 +217,15 @@ def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
 
 def hsv_tree_ancestor_mask(parent: torch.Tensor, anc_mask: Optional[torch.Tensor] = None,
                            stream=None) -> torch.Tensor:
-    """uint64 ancestor bitmask [B, N] of the draft trees in ``parent``."""
+    """Ancestor bitmask of the draft trees in ``parent``: 64-bit [B, N] for
+    N <= 64, else [B, N, ceil(N/64)] (word w: nodes 64w .. 64w+63)."""
     if parent.dtype != torch.int32 or parent.dim() != 2:
         raise ValueError("parent must be int32 [B, N]")
     B, N = parent.shape
     if anc_mask is None:
-        anc_mask = torch.empty((B, N), dtype=torch.int64, device=parent.device)
+        shape = (B, N) if N <= 64 else (B, N, mask_words(N))
+        anc_mask = torch.empty(shape, dtype=torch.int64, device=parent.device)
+    _check_mask(anc_mask, B, N)
     _check_dev(parent, anc_mask)
     _check(lib.hsv_tree_ancestor_mask(_ptr(parent), _ptr(anc_mask), B, N,
                                       _stream(stream, parent.device)), "hsv_tree_ancestor_mask")

@@ -114,6 +114,9 @@ __device__ __forceinline__ void wait_tile_and_sync(int later) {
 
 __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  // trees of more than 64 nodes: the mask of each of this workgroup's rows,
+  // as 32-bit words (word w holds nodes 32w .. 32w+31)
+  __shared__ uint32_t wide_mask[kNW * 32 * 8];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -244,7 +247,18 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
       const uint4 u = ok ? qv[qrow * (kD / 8) + 2 * ks + hf] : make_uint4(0, 0, 0, 0);
       qf[ks] = __builtin_bit_cast(bf16x8, u);
     }
-    if (tree) {
+    if (tree && P.anc_words > 1) {
+      // rows of this workgroup: their masks into LDS (zero past R)
+      const int rl = tid / 2;  // 512 threads: two per row, alternate words
+      const int rr = rc * (kNW * 32) + rl;
+      const int ii = rr < P.R ? rr / P.G : 0;
+      const uint64_t *src = P.anc + (static_cast<int64_t>(b) * P.N + ii) * P.anc_words;
+      for (int w = tid & 1; w < 4; w += 2) {
+        const uint64_t x = (rr < P.R && w < P.anc_words) ? src[w] : 0;
+        wide_mask[rl * 8 + 2 * w] = static_cast<uint32_t>(x);
+        wide_mask[rl * 8 + 2 * w + 1] = static_cast<uint32_t>(x >> 32);
+      }
+    } else if (tree) {
       if (P.anc) {
         anc_q = P.anc[static_cast<int64_t>(b) * P.N + i];
       } else {
@@ -261,6 +275,10 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
   asm volatile("" ::"v"(anc_q));
+  // the LDS mask words of wide trees are read by every wave (this barrier's
+  // wait for all memory operations costs nothing: the query loads above
+  // already wait for everything in flight)
+  if (tree && P.anc_words > 1) __syncthreads();
 
   // lane bases of the LDS reads (byte offsets inside a stage)
   const int k_base = (l32 >> 4) * 4096 + hf * 256 + (l32 & 15) * 16;
@@ -325,7 +343,16 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     const int room = t_end - base;  // keys inside the slot
     const int pre = c - base;       // prefix keys (always visible)
     uint32_t keep = pre <= 0 ? 0u : pre >= 32 ? ~0u : ((1u << pre) - 1u);
-    if (tree) {
+    if (tree && P.anc_words > 1) {
+      // bits [sh, sh + 32) of this row's N-bit mask, from the LDS words
+      const int sh = -pre;
+      const int a = sh >= 0 ? sh / 32 : -((31 - sh) / 32);  // floor(sh / 32)
+      const int o = sh - 32 * a;
+      const uint32_t *mw = wide_mask + (wave * 32 + l32) * 8;
+      const uint32_t lo = (a >= 0 && a < 8) ? mw[a] : 0u;
+      const uint32_t hi = (a + 1 >= 0 && a + 1 < 8) ? mw[a + 1] : 0u;
+      keep |= static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> o);
+    } else if (tree) {
       const int sh = -pre;  // draft node of bit 0
       keep |= sh >= 64 || sh <= -32 ? 0u
               : sh >= 0         ? static_cast<uint32_t>(anc_q >> sh)

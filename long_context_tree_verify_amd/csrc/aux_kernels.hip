@@ -20,6 +20,44 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t *parent, ui
   if (lane < n_draft) anc[static_cast<int64_t>(b) * n_draft + lane] = bad ? 0 : a;
 }
 
+// Ancestor bitmask of trees of 65 to 256 nodes: W = ceil(N/64) words per
+// node, word w holding nodes 64w .. 64w+63.  One 256-thread workgroup per
+// sequence; thread i walks its parent chain (parents in LDS; a valid array
+// strictly decreases along it, so at most i steps) into four word registers.
+// Every word of a sequence with an out-of-range parent is 0.
+__global__ __launch_bounds__(256) void tree_mask_wide_kernel(const int32_t *parent, uint64_t *anc,
+                                                             int n_draft) {
+  __shared__ int32_t par[256];
+  __shared__ int32_t bad;
+  const int b = blockIdx.x, i = threadIdx.x;
+  if (i == 0) bad = 0;
+  __syncthreads();
+  if (i < n_draft) {
+    const int p = parent[static_cast<int64_t>(b) * n_draft + i];
+    par[i] = p;
+    if (p < -1 || p >= i) atomicOr(&bad, 1);
+  }
+  __syncthreads();
+  if (i >= n_draft) return;
+  uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+  if (!bad) {
+    for (int j = i; j >= 0; j = par[j]) {
+      const uint64_t bit = uint64_t{1} << (j & 63);
+      const int wi = j >> 6;
+      w0 |= wi == 0 ? bit : 0;
+      w1 |= wi == 1 ? bit : 0;
+      w2 |= wi == 2 ? bit : 0;
+      w3 |= wi == 3 ? bit : 0;
+    }
+  }
+  const int W = (n_draft + 63) / 64;
+  uint64_t *row = anc + (static_cast<int64_t>(b) * n_draft + i) * W;
+  row[0] = w0;
+  if (W > 1) row[1] = w1;
+  if (W > 2) row[2] = w2;
+  if (W > 3) row[3] = w3;
+}
+
 // --------------------------------------------------------------------------
 // Log-sum-exp merge (LongSpec section 2.C: exact combination of the parts).
 // One wave per output row.  A part's row of D floats is read by L = D/4
@@ -249,7 +287,10 @@ __global__ __launch_bounds__(256) void validate_kernel(Plan P) {
 
 hipError_t launch_tree_mask(const int32_t *parent, uint64_t *anc, int batch, int n_draft,
                             hipStream_t s) {
-  hipLaunchKernelGGL(tree_mask_kernel, dim3(batch), dim3(64), 0, s, parent, anc, n_draft);
+  if (n_draft > 64)
+    hipLaunchKernelGGL(tree_mask_wide_kernel, dim3(batch), dim3(256), 0, s, parent, anc, n_draft);
+  else
+    hipLaunchKernelGGL(tree_mask_kernel, dim3(batch), dim3(64), 0, s, parent, anc, n_draft);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxSplits = 256;
 constexpr int kTile = 64;
+constexpr int kMaxDraft = 256;  // draft nodes per sequence (masks of up to 4 words)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -30,7 +31,7 @@ hsv_status check_desc(const hsv_verify_desc *d, bool sparse) {
     if (bs < 64 || bs > (1 << 20) || (bs & (bs - 1)) || d->kv_capacity % bs) return HSV_ERR_SHAPE;
     if (sparse || (d->flags & HSV_FLAG_NO_PREFIX)) return HSV_ERR_UNSUPPORTED;
   }
-  if (d->batch < 1 || d->n_draft < 1 || d->n_draft > 64) return HSV_ERR_SHAPE;
+  if (d->batch < 1 || d->n_draft < 1 || d->n_draft > kMaxDraft) return HSV_ERR_SHAPE;
   if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads) return HSV_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return HSV_ERR_UNSUPPORTED;
   if (d->max_ctx < 0 || d->kv_capacity < 1) return HSV_ERR_SHAPE;
@@ -66,6 +67,8 @@ size_t workspace_bytes(const Plan &p) {
   off += align_up(rows * sizeof(float));                           // lse_part
   if (p.part_f16) off += align_up(rows * sizeof(float));            // o_scale
   off += kAlign;                                                   // error word
+  if (p.anc_words > 1)                                             // wide masks
+    off += align_up(static_cast<size_t>(p.B) * p.N * p.anc_words * sizeof(uint64_t));
   return off;
 }
 
@@ -82,6 +85,7 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
   p->G = d->n_q_heads / d->n_kv_heads;
   p->D = d->head_dim;
   p->R = p->G * p->N;
+  p->anc_words = (p->N + 63) / 64;
   p->cap = d->kv_capacity;
   p->n_sel = sparse ? d->n_sel : 0;
   p->max_ctx = d->max_ctx;
@@ -126,6 +130,8 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
   p->unified = p->kernel == kKernDma256 || p->kernel == kKernDmaSmall;
   const bool paged = d->block_size > 0;
   if (paged && !p->unified) return HSV_ERR_UNSUPPORTED;
+  // trees of more than 64 nodes: the 256-row kernel only (multi-word masks)
+  if (p->N > 64 && with_tree && p->kernel != kKernDma256) return HSV_ERR_UNSUPPORTED;
   if (p->unified) {
     // One key range per (b, kv head): prefix (or index set) then draft rows.  One workgroup
     // per CU: as many splits as fit in one round of the CUs (splits of a
@@ -209,6 +215,8 @@ void carve_workspace(Plan *p, void *ws) {
     base += align_up(rows * sizeof(float));
   }
   p->err = reinterpret_cast<int32_t *>(base);
+  base += kAlign;
+  p->anc_ws = p->anc_words > 1 ? reinterpret_cast<uint64_t *>(base) : nullptr;
 }
 
 hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, const void *k,
@@ -261,6 +269,13 @@ hsv_status run_verify(const hsv_verify_desc *d, bool sparse, const void *q, cons
       return HSV_ERR_HIP;
     if (hipStreamSynchronize(stream) != hipSuccess) return HSV_ERR_HIP;
     if (host_err) return HSV_ERR_DEVICE_CHECK;
+  }
+  // trees of more than 64 nodes given as parents: their multi-word masks
+  // first, into the workspace
+  if (p.has_tree && p.anc_words > 1 && p.parent) {
+    if (launch_tree_mask(p.parent, p.anc_ws, p.B, p.N, stream) != hipSuccess) return HSV_ERR_HIP;
+    p.anc = p.anc_ws;
+    p.parent = nullptr;
   }
   const uint32_t phase = d->flags & (HSV_FLAG_PHASE_PARTIALS | HSV_FLAG_PHASE_MERGE);
   const bool run_partials = phase != HSV_FLAG_PHASE_MERGE;
@@ -327,7 +342,7 @@ hsv_status hsv_verify_attn_paged(const hsv_verify_desc *d, const void *q, const 
 hsv_status hsv_tree_ancestor_mask(const int32_t *parent, uint64_t *anc_mask, int32_t batch,
                                   int32_t n_draft, hipStream_t stream) {
   if (!parent || !anc_mask) return HSV_ERR_NULL;
-  if (batch < 1 || n_draft < 1 || n_draft > 64) return HSV_ERR_SHAPE;
+  if (batch < 1 || n_draft < 1 || n_draft > kMaxDraft) return HSV_ERR_SHAPE;
   return launch_tree_mask(parent, anc_mask, batch, n_draft, stream) == hipSuccess ? HSV_OK
                                                                                   : HSV_ERR_HIP;
 }

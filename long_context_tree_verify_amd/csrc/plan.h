@@ -35,7 +35,8 @@ struct Plan {
   const void *v;
   const int32_t *ctx_lens;
   const int32_t *parent;    // NULL when anc is given (or no tree part)
-  const uint64_t *anc;      // NULL when parent is given
+  const uint64_t *anc;      // NULL when parent is given; [B][N][anc_words]
+  uint64_t *anc_ws;         // workspace for the masks of trees of more than 64 nodes
   const int32_t *kv_idx;    // sparse prefix, else NULL
   const int32_t *block_table; // paged cache: [B][max_blocks] pool block of each
                               // logical block of block_size rows; else NULL
@@ -66,6 +67,7 @@ struct Plan {
   int32_t kgroups;          // partial results per slot workgroup
   int32_t n_parts;          // n_slots * kgroups
   int32_t row_chunks;       // workgroups per (slot, b, kv head) along rows
+  int32_t anc_words;        // 64-bit words per node's mask: ceil(N / 64)
   int32_t block_shift;      // paged: log2(block_size)
   int32_t max_blocks;       // paged: cap / block_size (columns of block_table)
   int32_t n_pool_blocks;    // paged: pool blocks in k and v

@@ -104,15 +104,17 @@ def block_masks(n: int, block: int) -> np.ndarray:
     """Visibility masks of block-parallel drafting (FlexDraft page, attention
     tuning): the n draft tokens form consecutive blocks of `block` tokens;
     a token sees every token of its own block, earlier and later ones alike,
-    and none of the other blocks.  uint64 [n], bit j = token j visible."""
-    if not 1 <= n <= 64:
-        raise ValueError("at most 64 draft tokens per mask word")
+    and none of the other blocks.  uint64 [n] for n <= 64 (bit j = token j
+    visible), else [n, ceil(n/64)] (word w holds tokens 64w .. 64w+63)."""
+    if not 1 <= n <= 256:
+        raise ValueError("1 to 256 draft tokens")
+    W = (n + 63) // 64
     blk = np.arange(n) // block
-    out = np.zeros(n, dtype=np.uint64)
+    out = np.zeros((n, W), dtype=np.uint64)
     for i in range(n):
         for j in np.flatnonzero(blk == blk[i]):
-            out[i] |= np.uint64(1) << np.uint64(j)
-    return out
+            out[i, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    return out[:, 0] if W == 1 else out
 
 
 def random_masks(rng: np.random.Generator, batch: int, n: int, density: float = 0.5):

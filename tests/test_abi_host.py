@@ -71,7 +71,9 @@ def test_workspace_size_valid_and_monotone(hsv):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(n_draft=0), 2), (dict(n_draft=65), 2), (dict(batch=0), 2),
+    (dict(n_draft=0), 2), (dict(n_draft=257), 2), (dict(batch=0), 2),
+    (dict(n_draft=65, head_dim=64, max_ctx=32000), 3),
+    (dict(n_draft=65, n_q_heads=8, max_ctx=32000), 3), (dict(n_draft=256, max_ctx=32000), 0),
     (dict(n_q_heads=30), 2), (dict(n_kv_heads=0), 2), (dict(head_dim=96), 3),
     (dict(max_ctx=32769), 2), (dict(max_ctx=-1), 2), (dict(num_splits=257), 2),
     (dict(num_splits=-1), 2), (dict(in_dtype=7), 3), (dict(out_dtype=2), 3),
@@ -106,7 +108,7 @@ def test_verify_rejects_null_and_workspace_errors(hsv):
     assert _call_dense(hsv, d, k=ctypes.c_void_p(0x10002)) == hsv.HSV_ERR_SHAPE
     assert hsv.lib.hsv_verify_attn(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                                    ctypes.c_size_t(1 << 20), None) == hsv.HSV_ERR_NULL
-    bad = _desc(hsv, n_draft=65)
+    bad = _desc(hsv, n_draft=257)
     assert _call_dense(hsv, bad, ws_bytes=1 << 30) == hsv.HSV_ERR_SHAPE
     # a dense call must not carry n_sel; the tree may be left out without parents
     assert _call_dense(hsv, _desc(hsv, n_sel=10), ws_bytes=1 << 30) == hsv.HSV_ERR_SHAPE
@@ -127,7 +129,7 @@ def test_sparse_rejects_missing_indices(hsv):
 def test_small_entry_points_reject_bad_arguments(hsv):
     lib = hsv.lib
     assert lib.hsv_tree_ancestor_mask(None, FAKE, 1, 8, None) == hsv.HSV_ERR_NULL
-    assert lib.hsv_tree_ancestor_mask(FAKE, FAKE, 1, 65, None) == hsv.HSV_ERR_SHAPE
+    assert lib.hsv_tree_ancestor_mask(FAKE, FAKE, 1, 257, None) == hsv.HSV_ERR_SHAPE
     assert lib.hsv_tree_ancestor_mask(FAKE, FAKE, 0, 8, None) == hsv.HSV_ERR_SHAPE
     assert lib.hsv_gather_kv(FAKE, FAKE, None, FAKE, FAKE, 1, 1, 10, 128, 4, 1,
                              None) == hsv.HSV_ERR_NULL
