@@ -383,6 +383,67 @@ def measure_recall(hsv, dev, steps: int):
             "rows": int(arr.numel())}
 
 
+def measure_wide_tree(hsv, dev, steps: int, out_dtype):
+    """The 32k-context step with a 256-node draft tree (masks of four 64-bit
+    words, 1024 grouped rows per KV head): whole steps in a graph, HIP events
+    on the capture stream.  At 1024 rows the step does 4x the MFMA work per
+    KV byte of the 64-node tree, so the matrix cores bound it."""
+    import numpy as np
+    import torch
+
+    import synth
+    inp = synth.make_inputs("tree32k", n_draft=256, max_depth=16)
+    wl = inp.wl
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k0, v0 = up(inp.q), up(inp.k), up(inp.v)
+    cache_bytes = 2 * k0.numel() * k0.element_size()
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / cache_bytes) + 1)
+    ks, vs = [k0] + [k0.clone() for _ in range(copies - 1)], [v0] + [v0.clone()
+                                                                      for _ in range(copies - 1)]
+    ctx = torch.from_numpy(inp.ctx_lens).to(dev)
+    parent = torch.from_numpy(inp.parent).to(dev)
+    B, N, Hq, D = q.shape
+    o = torch.empty((B, N, Hq, D), dtype=out_dtype, device=dev)
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    max_ctx = int(inp.ctx_lens.max())
+    desc = hsv.make_desc(batch=B, n_draft=N, n_q_heads=Hq, n_kv_heads=wl.n_kv_heads,
+                         head_dim=D, kv_capacity=k0.shape[2], max_ctx=max_ctx,
+                         in_dtype=hsv.HSV_BF16,
+                         out_dtype=hsv.HSV_BF16 if out_dtype == torch.bfloat16 else hsv.HSV_F32)
+    ws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+
+    def call(j):
+        hsv.hsv_verify_attn(q, ks[j % copies], vs[j % copies], ctx, parent, max_ctx=max_ctx,
+                            out_dtype=out_dtype, o=o, lse=lse, workspace=ws, stream=None)
+
+    for j in range(3):
+        call(j)
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for j in range(steps):
+            call(j)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes, flops = kv_bytes(inp), step_flops(inp)
+    return {"workload": f"tree32k with a 256-node tree (depth <= 16, branching <= 4), "
+                        f"{wl.group * N} grouped rows per KV head",
+            "us_per_step": round(us, 2), "kv_read_bytes": nbytes, "flop": flops,
+            "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_util": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +453,8 @@ def main(argv=None) -> int:
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-wide", action="store_true",
+                    help="skip the 256-node tree measurement")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache measurement")
     ap.add_argument("--no-selection", action="store_true",
@@ -567,6 +630,9 @@ def main(argv=None) -> int:
     if inp.kv_idx is None and bf and wl.head_dim == 128 and not args.no_paged:
         log("bench: timing the paged-cache step")
         result["paged"] = measure_paged(hsv, dev, inp, args.steps, out_dtype)
+    if wl.name == "tree32k" and not args.no_wide:
+        log("bench: timing the 256-node tree step")
+        result["wide_tree"] = measure_wide_tree(hsv, dev, args.steps, out_dtype)
     log("bench: timing the accepted-path cache update")
     result["accept"] = measure_accept(hsv, dev, inp, args.steps)
     if not args.no_selection:
