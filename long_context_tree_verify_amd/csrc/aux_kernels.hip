@@ -109,8 +109,11 @@ __device__ __forceinline__ void merge_row(const void *o_parts, const float *lse_
     const int p = min(S * u + sub, n_parts - 1);  // stays in bounds
     v[u] = load4<F16>(o_parts, o0 + p * ostride);
   }
-  // LSEs: parts 0..63 in flight with the rows, the rest (if any) by a loop
+  // LSEs (and row scales): parts 0..63 in flight with the rows, the rest (if
+  // any) by a loop
   const float l0 = lane < n_parts ? lp[static_cast<int64_t>(lane) * part_stride_rows] : kNegInf;
+  const float s0 =
+      (F16 && lane < n_parts) ? sp[static_cast<int64_t>(lane) * part_stride_rows] : 0.f;
   float m = l0;
   for (int p = lane + kWave; p < n_parts; p += kWave) m = fmaxf(m, lp[p * part_stride_rows]);
   m = wave_max(m);
@@ -135,17 +138,16 @@ __device__ __forceinline__ void merge_row(const void *o_parts, const float *lse_
       }
     }
     // the LSE (and scale) of part p0 + j sits in lane base + j
-    float lsrc = l0;
+    float lsrc = l0, ssrc = s0;
     int base = p0;
-    int psrc = lane;
     if (p0 >= kWave) {
-      psrc = p0 + (lane & (kMergeGroup - 1));
+      const int psrc = p0 + (lane & (kMergeGroup - 1));
       lsrc = psrc < n_parts ? lp[psrc * part_stride_rows] : kNegInf;
+      if constexpr (F16) ssrc = sp[min(psrc, n_parts - 1) * part_stride_rows];
       base = 0;
     }
     float wsrc = fast_exp2((lsrc - lse) * kLog2e);
-    if constexpr (F16)
-      wsrc = lsrc > kNegInf ? wsrc * sp[min(psrc, n_parts - 1) * part_stride_rows] : 0.f;
+    if constexpr (F16) wsrc = lsrc > kNegInf ? wsrc * ssrc : 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float w = 0.f;
