@@ -49,6 +49,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -114,8 +116,8 @@ __device__ __forceinline__ void wait_tile_and_sync(int later) {
 
 __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  // trees of more than 64 nodes: the mask of each of this workgroup's rows,
-  // as 32-bit words (word w holds nodes 32w .. 32w+31)
+  // the ancestor mask of each of this workgroup's rows, as 32-bit words
+  // (word w holds draft nodes 32w .. 32w+31; zero past the tree's words)
   __shared__ uint32_t wide_mask[kNW * 32 * 8];
 
   const int tid = threadIdx.x;
@@ -189,19 +191,11 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   lds_char *const lds = (lds_char *)(smem);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
-  // ---- DMA lane offsets ------------------------------------------------------
+  // ---- DMA of one tile --------------------------------------------------------
   // K block blk: lane i carries key (blk/4)*16 + i%16, chunk (blk%4)*4 + i/16;
   // V block blk: key (blk/4)*16 + i/4, chunk (blk%4)*4 + i%4.
-  int krel[kBlocksPerWave], vrel[kBlocksPerWave];
-  uint32_t kch[kBlocksPerWave], vch[kBlocksPerWave];
-#pragma unroll
-  for (int bw = 0; bw < kBlocksPerWave; ++bw) {
-    const int blk = wave * kBlocksPerWave + bw;
-    krel[bw] = (blk >> 2) * 16 + (lane & 15);
-    kch[bw] = ((blk & 3) * 4 + (lane >> 4)) * 16;
-    vrel[bw] = (blk >> 2) * 16 + (lane >> 2);
-    vch[bw] = ((blk & 3) * 4 + (lane & 3)) * 16;
-  }
+  // The lane offsets are recomputed for every tile (a few VALU operations)
+  // rather than held in registers through the main loop.
   // This thread's DMA of tile j into stage j % kStages.
   auto issue_tile = [&](const int j) {
     const int row_first = t_begin + j * kTK;
@@ -210,33 +204,31 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     const char *kt = kbytes + off;
     const char *vt = vbytes + off;
     const uint32_t st = lds0 + (j % kStages) * kStageBytes;
-    if (lim >= kTK - 1) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // not hoisted out of the loop
+    const bool full = lim >= kTK - 1;
 #pragma unroll
-      for (int bw = 0; bw < kBlocksPerWave; ++bw) {
-        const uint32_t blk_off = (wave * kBlocksPerWave + bw) * 1024;
-        dma16(kt, krel[bw] * kRowBytes + kch[bw], st + blk_off);
-        dma16(vt, vrel[bw] * kRowBytes + vch[bw], st + kTileBytes + blk_off);
-      }
-    } else {
-#pragma unroll
-      for (int bw = 0; bw < kBlocksPerWave; ++bw) {
-        const uint32_t blk_off = (wave * kBlocksPerWave + bw) * 1024;
-        dma16(kt, min(krel[bw], lim) * kRowBytes + kch[bw], st + blk_off);
-        dma16(vt, min(vrel[bw], lim) * kRowBytes + vch[bw], st + kTileBytes + blk_off);
-      }
+    for (int bw = 0; bw < kBlocksPerWave; ++bw) {
+      const int blk = wave * kBlocksPerWave + bw;
+      const uint32_t blk_off = blk * 1024;
+      const int krel = (blk >> 2) * 16 + (ln & 15);
+      const int vrel = (blk >> 2) * 16 + (ln >> 2);
+      const uint32_t kch = ((blk & 3) * 4 + (ln >> 4)) * 16;
+      const uint32_t vch = ((blk & 3) * 4 + (ln & 3)) * 16;
+      dma16(kt, (full ? krel : min(krel, lim)) * kRowBytes + kch, st + blk_off);
+      dma16(vt, (full ? vrel : min(vrel, lim)) * kRowBytes + vch, st + kTileBytes + blk_off);
     }
   };
 
-  // prologue: tiles 0 .. kAhead-1 in flight, issued before the query loads so
-  // the two latencies overlap
-#pragma unroll
-  for (int j = 0; j < kAhead; ++j)
-    if (j < n_tiles) issue_tile(j);
+  // prologue: tile 0 in flight before the query loads, so the two latencies
+  // overlap; the later prologue tiles are issued once the query has landed
+  // (the wait for the query also covers every DMA issued before it, and at
+  // start-up all workgroups share the HBM queue)
+  issue_tile(0);
 
   // ---- this lane's query (B operand of S^T = K.Q^T), tree mask word --------
   const uint4 *qv = static_cast<const uint4 *>(P.q);
   bf16x8 qf[8];
-  uint64_t anc_q = 0;
   {
     const bool ok = r < P.R;
     const int i = ok ? r / P.G : 0;
@@ -259,6 +251,9 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
         wide_mask[rl * 8 + 2 * w + 1] = static_cast<uint32_t>(x >> 32);
       }
     } else if (tree) {
+      // one 64-bit word per row: this wave's rows into the same LDS layout
+      // (words 2..7 zero), written and read by this wave only
+      uint64_t anc_q;
       if (P.anc) {
         anc_q = P.anc[static_cast<int64_t>(b) * P.N + i];
       } else {
@@ -267,18 +262,25 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
                                           &bad);
         anc_q = shfl_u64(a, i);
       }
+      uint32_t *mw = wide_mask + (wave * 32 + l32) * 8 + 4 * hf;
+      mw[0] = hf == 0 ? static_cast<uint32_t>(anc_q) : 0u;
+      mw[1] = hf == 0 ? static_cast<uint32_t>(anc_q >> 32) : 0u;
+      mw[2] = 0u;
+      mw[3] = 0u;
     }
   }
 
   // Consume the query (and tree) loads now.  The compiler does not count the
-  // DMA, so its wait here is vmcnt(0): the prologue tiles have landed too.
+  // DMA, so its wait here is vmcnt(0): tile 0 has landed too.
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
-  asm volatile("" ::"v"(anc_q));
   // the LDS mask words of wide trees are read by every wave (this barrier's
   // wait for all memory operations costs nothing: the query loads above
   // already wait for everything in flight)
   if (tree && P.anc_words > 1) __syncthreads();
+#pragma unroll
+  for (int j = 1; j < kAhead; ++j)
+    if (j < n_tiles) issue_tile(j);
 
   // lane bases of the LDS reads (byte offsets inside a stage)
   const int k_base = (l32 >> 4) * 4096 + hf * 256 + (l32 & 15) * 16;
@@ -325,6 +327,17 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
                                                6, 7);
   };
 
+  // The half `half` (keys 16*half .. +15 of the block) of the V^T operands.
+  auto read_v_half = [&](lds_char *const st, const int kb, const int half, bf16x8 (&va)[4][2]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      lds_char *vp = st + v_base + (kb * 2 + half) * 4096 + db * 1024;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp + 512));
+      va[db][half] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+
   auto to_bf16 = [&](const float (&p)[16], bf16x8 (&pb)[2]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -343,7 +356,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     const int room = t_end - base;  // keys inside the slot
     const int pre = c - base;       // prefix keys (always visible)
     uint32_t keep = pre <= 0 ? 0u : pre >= 32 ? ~0u : ((1u << pre) - 1u);
-    if (tree && P.anc_words > 1) {
+    if (tree) {
       // bits [sh, sh + 32) of this row's N-bit mask, from the LDS words
       const int sh = -pre;
       const int a = sh >= 0 ? sh / 32 : -((31 - sh) / 32);  // floor(sh / 32)
@@ -352,11 +365,6 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
       const uint32_t lo = (a >= 0 && a < 8) ? mw[a] : 0u;
       const uint32_t hi = (a + 1 >= 0 && a + 1 < 8) ? mw[a + 1] : 0u;
       keep |= static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> o);
-    } else if (tree) {
-      const int sh = -pre;  // draft node of bit 0
-      keep |= sh >= 64 || sh <= -32 ? 0u
-              : sh >= 0         ? static_cast<uint32_t>(anc_q >> sh)
-                                : static_cast<uint32_t>(anc_q << (-sh));
     }
     keep &= room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
 #pragma unroll
@@ -421,53 +429,114 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   };
 
   // Software pipeline over 32-key blocks t = 0 .. 2*n_tiles - 1 (block t is
-  // half t % 2 of tile t / 2).  Step t issues the QK^T MFMAs of block t+1
-  // in the same branch-free stretch as block t's exponentials, so the matrix
-  // cores and the VALU work side by side within one wave; then block t's
-  // slow-path check and its P.V.  Tile j sits in stage j % kStages; the
-  // barrier before the first block of tile j+1 (at step 2j+1) also tells
-  // every wave that the others are done with tile j-1, whose stage the DMA
-  // of tile j+1+kAhead then reuses.  The last step's "next block" reads a
-  // stage that holds an older tile: its scores are never used.
+  // half t % 2 of tile t / 2).  Step t computes block t's probabilities
+  // while the matrix cores run the QK^T MFMAs of block t+1 and the P.V MFMAs
+  // of block t-1, alternating, so a wave keeps both the VALU and the matrix
+  // core busy and no MFMA waits on the one before it.  Every LDS read of a
+  // step is consumed inside that step.  Tile j sits in stage j % kStages;
+  // the barrier of step 2j+1 (before the first read of tile j+1) also tells
+  // every wave that the others are done with step 2j, the last reader of
+  // tile j-1, whose stage the DMA of tile j+1+kAhead then reuses.  The last
+  // step's "next block" reads a stage that holds an older tile: its scores
+  // are never used.
+  //
+  // The probabilities of block t are taken against the running reference
+  // m_run; when the slow path moves the reference, the accumulators already
+  // hold P.V of blocks up to t-1 and are rescaled with l_run, and block t's
+  // probabilities (carried to step t+1 in pb_prev) use the new reference.
   const int n_blocks = 2 * n_tiles;
-  wait_tile_and_sync(min(n_tiles - 1, kAhead - 1));
-  if (kAhead < n_tiles) issue_tile(kAhead);
-  floatx16 s_cur;
-  {
-    bf16x8 ka[8];
-    read_k(lds, 0, ka);
-    qk_mfma(ka, s_cur);
-  }
-  for (int t = 0; t < n_blocks; ++t) {
-    const int j = t >> 1, kb = t & 1;
-    lds_char *const st = lds + (j % kStages) * kStageBytes;
+  const int s_mask = kStages * kStageBytes - 1;
+  // stage byte offset of block tb's tile (stage sizes are a power of two)
+  auto stage_of = [&](const int tb) { return lds + (((tb >> 1) * kStageBytes) & s_mask); };
+  bf16x8 pb_prev[2];
+
+  auto step = [&](const int t, floatx16 &s_cur, floatx16 &s_nxt, auto with_pv) {
+    constexpr bool kPV = decltype(with_pv)::value;
     const int t0 = t_begin + t * 32;
-    if (kb == 1 && t + 1 < n_blocks) {
-      wait_tile_and_sync(min(n_tiles - 2 - j, kAhead - 1));
-      if (j + 1 + kAhead < n_tiles) issue_tile(j + 1 + kAhead);
-    }
-    // the next block's K operands first (its MFMAs wait on them), then this
-    // block's V operands (needed only after the softmax)
+    // the next block's K operands, then the previous block's V^T operands
     bf16x8 ka[8];
-    read_k(lds + (((t + 1) >> 1) % kStages) * kStageBytes, (t + 1) & 1, ka);
+    read_k(stage_of(t + 1), (t + 1) & 1, ka);
+    // V^T operands: the first halves now, the second halves (used by the
+    // last four P.V MFMAs) from the third MFMA pair on, to bound the live
+    // registers
     bf16x8 va[4][2];
-    read_v(st, kb, va);
+    lds_char *const vst = stage_of(t - 1);
+    const int vkb = (t - 1) & 1;
+    if constexpr (kPV) read_v_half(vst, vkb, 0, va);
     if (t0 + 32 > mask_from) apply_mask(s_cur, t0);
-    floatx16 s_nxt;
+    uint32_t pw[8];  // probabilities 2w, 2w+1 as a bf16 pair
+    float sum = 0.f;
+    s_nxt = floatx16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s_nxt, 0, 0, 0);
+      if constexpr (kPV) {
+        if (ks == 2) read_v_half(vst, vkb, 1, va);
+      }
+      if constexpr (kPV)
+        o_acc[ks & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 3][ks >> 2],
+                                                                pb_prev[ks >> 2], o_acc[ks & 3],
+                                                                0, 0, 0);
+      floatx2 x;
+      x[0] = fast_exp2(fmaf(s_cur[2 * ks], cs, -m_run));
+      x[1] = fast_exp2(fmaf(s_cur[2 * ks + 1], cs, -m_run));
+      sum += x[0];
+      sum += x[1];
+      pw[ks] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    }
+    // Issue order: a few exponentials while the K operands arrive, then each
+    // QK^T MFMA and each P.V MFMA followed by three VALU operations, and the
+    // second half of the V^T reads after the third pair.
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      if constexpr (kPV) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        if (ks == 2) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      }
+    }
     bf16x8 pb[2];
-    qk_mfma(ka, s_nxt);
-    float sum = fast_p(s_cur, pb);
+    pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
     // Keep the conversion ahead of the branch: otherwise the compiler sinks
     // it into the fast path, the fp32 probabilities stay live across the
-    // join with the slow path, and the merge copies the accumulators into
-    // new registers (spills, whose scratch loads would also wait on the DMA
-    // in flight).
+    // join with the slow path, and the merge copies registers (spills, whose
+    // scratch loads would also wait on the DMA in flight).
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
     if (__builtin_expect(__any(!(sum <= kSumLimit) || m_run == kNegInf), 0))
       slow_p(s_cur, pb, sum);
     l_run += sum;
-    pv(va, pb);
-    s_cur = s_nxt;
+    pb_prev[0] = pb[0];
+    pb_prev[1] = pb[1];
+  };
+  using no_pv = std::integral_constant<bool, false>;
+  using has_pv = std::integral_constant<bool, true>;
+
+  wait_tile_and_sync(min(n_tiles - 1, kAhead - 1));
+  if (kAhead < n_tiles) issue_tile(kAhead);
+  floatx16 s_a, s_b;  // scores of the even and the odd blocks
+  {
+    bf16x8 ka[8];
+    read_k(lds, 0, ka);
+    qk_mfma(ka, s_a);
+  }
+  step(0, s_a, s_b, no_pv{});
+  for (int j = 0; j + 1 < n_tiles; ++j) {
+    // step 2j+1 reads the K operands of tile j+1
+    wait_tile_and_sync(min(n_tiles - 2 - j, kAhead - 1));
+    if (j + 1 + kAhead < n_tiles) issue_tile(j + 1 + kAhead);
+    step(2 * j + 1, s_b, s_a, has_pv{});
+    step(2 * j + 2, s_a, s_b, has_pv{});
+  }
+  step(n_blocks - 1, s_b, s_a, has_pv{});
+  {
+    // P.V of the last block
+    bf16x8 va[4][2];
+    read_v(stage_of(n_blocks - 1), 1, va);
+    pv(va, pb_prev);
   }
 
   // ---- epilogue --------------------------------------------------------------
