@@ -112,6 +112,31 @@ def test_dma_path_edges(hsv, gpu, over, wl):
         assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"splits={splits}")
 
 
+# Keys scored far above everything before them (32x the row, so the score
+# jumps by many log2 units), placed mid-range, at the last row of a 32-key
+# block, in the last prefix block and among the draft rows: the softmax's slow
+# path then rescales accumulators that already hold the P.V of earlier blocks,
+# including the block just before, whose P.V the 256-row kernel adds one step
+# late.
+def test_dma_rescale_mid_range(hsv, gpu):
+    import dataclasses
+    inp = cached_inputs("tree32k", (("ctx", (3000, 3000)),))
+    assert inp.k.dtype == np.uint16
+    c = int(inp.ctx_lens[0])
+    rows = [37, 700, 1055, 1535, c - 1, c + 5]
+    k = inp.k.copy()
+    f = (k[:, :, rows, :].astype(np.uint32) << 16).view(np.float32) * np.float32(32.0)
+    k[:, :, rows, :] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    spiked = dataclasses.replace(inp, k=k)
+    dev = device_inputs(spiked, gpu)
+    o_ref, l_ref = _oracle_all(spiked)
+    base_ref = _oracle_all(inp)[1]
+    assert float(np.max(l_ref - base_ref)) > 10.0   # the spikes dominate many rows
+    for splits in (1, 3, 0):
+        o, lse = run_hip(hsv, spiked, dev, num_splits=splits)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"splits={splits}")
+
+
 def test_tiny_fp32_is_tight(hsv, gpu):
     inp = cached_inputs("tiny_tree")
     dev = device_inputs(inp, gpu)
