@@ -28,9 +28,9 @@
 //    nor guards LDS reads against it; waits are explicit instead: one asm
 //    statement does s_waitcnt vmcnt(n) for this thread's own DMA and then
 //    s_barrier, with a memory clobber so no LDS access moves across it.  No
-//    full memory fence, so later tiles stay in flight.  The query loads are
-//    consumed before the first DMA is issued, so the compiler's own vmcnt
-//    waits never cover an unknown DMA count.  M0 (the LDS base of the DMA) is
+//    full memory fence, so later tiles stay in flight.  The query rows take
+//    the same DMA path (into two stages that tiles 2 and 3 reuse later), so
+//    the first tiles are in flight with them from the start.  M0 (the LDS base of the DMA) is
 //    set inside the same asm statement; the kernel uses M0 for nothing else.
 //  * The V^T operands of a key block are read before its softmax, so their
 //    LDS latency overlaps the exponentials.
@@ -73,6 +73,13 @@ constexpr int kBlocksPerWave = kBlocks / kNW;  // per wave, for K and again for 
 constexpr int kDmaPerTile = 2 * kBlocksPerWave;  // DMA instructions per thread per tile
 // Epilogue staging: every wave's 32 x 128 fp16 partial, rows padded by 16 B.
 constexpr int kEpiRowStride = kD * 2 + 16;
+// Query staging: the workgroup's 256 query rows (64 KB) in stages 2 and 3,
+// which the tiles first reuse after the first barrier.  Inside a row, 16-byte
+// chunk c sits at position c ^ (row % 16), so a 16-lane read of one chunk
+// from 16 rows touches 16 distinct bank groups.
+constexpr int kQOff = 2 * kStageBytes;
+static_assert(kQOff + kNW * 32 * kRowBytes <= kStages * kStageBytes, "query staging");
+static_assert(kAhead == 2, "the prologue issues tiles 0 and 1 with the query");
 constexpr int kSmemBytes = kStages * kStageBytes > kNW * 32 * kEpiRowStride
                                ? kStages * kStageBytes
                                : kNW * 32 * kEpiRowStride;
@@ -220,24 +227,48 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     }
   };
 
-  // prologue: tile 0 in flight before the query loads, so the two latencies
-  // overlap; the later prologue tiles are issued once the query has landed
-  // (the wait for the query also covers every DMA issued before it, and at
-  // start-up all workgroups share the HBM queue)
+  // prologue: this wave's 32 query rows, then tiles 0 and 1, all by DMA, so
+  // the first tiles need not wait for the query to land.  Each 1 KB DMA
+  // instruction carries four rows; lane l takes chunk (l % 16) ^ (row % 16)
+  // of row 4j + l / 16, which lands at position l % 16 of that row.  Rows
+  // past R fetch row 0 of the group (a real entry) and are zeroed on reading.
+  // The paged block table is read first (issue_tile needs it), so no
+  // compiler wait for it covers the query DMA.
+  asm volatile("" ::"v"(ptab));
+  {
+    const char *qb = static_cast<const char *>(P.q) +
+                     static_cast<int64_t>(b) * P.N * P.Hq * kRowBytes;
+    const uint32_t qlds = lds0 + kQOff + (wave * 32) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rw = 4 * j + (lane >> 4);  // row inside the wave's 32
+      const int rr = row_base + rw;
+      const int rv = rr < P.R ? rr : 0;
+      const int qi = rv / P.G, qh = g * P.G + rv % P.G;
+      const uint32_t off = static_cast<uint32_t>((qi * P.Hq + qh) * kRowBytes) +
+                           static_cast<uint32_t>((((lane & 15) ^ (rw & 15))) * 16);
+      dma16(qb, off, qlds + j * 1024);
+    }
+  }
   issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
+  // the query DMA was issued first: it has landed once at most the tiles'
+  // four (or eight) instructions are outstanding
+  if (n_tiles > 1)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 
   // ---- this lane's query (B operand of S^T = K.Q^T), tree mask word --------
-  const uint4 *qv = static_cast<const uint4 *>(P.q);
   bf16x8 qf[8];
   {
     const bool ok = r < P.R;
     const int i = ok ? r / P.G : 0;
-    const int h = g * P.G + (ok ? r % P.G : 0);
-    const int64_t qrow = (static_cast<int64_t>(b) * P.N + i) * P.Hq + h;
+    lds_char *const qrow_lds = lds + kQOff + (wave * 32 + l32) * kRowBytes;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint4 u = ok ? qv[qrow * (kD / 8) + 2 * ks + hf] : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8, u);
+      const bf16x8 x = *(const lds_bf16x8 *)(qrow_lds + (((2 * ks + hf) ^ (l32 & 15)) * 16));
+      qf[ks] = ok ? x : bf16x8{};
     }
     if (tree && P.anc_words > 1) {
       // rows of this workgroup: their masks into LDS (zero past R)
@@ -270,17 +301,17 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     }
   }
 
-  // Consume the query (and tree) loads now.  The compiler does not count the
-  // DMA, so its wait here is vmcnt(0): tile 0 has landed too.
+  // Consume the query (and tree) reads now: every wave is done with the
+  // query staging before the first barrier, after which tile 2 reuses it.
+  // (Tree masks are read with ordinary loads, which the compiler waits for
+  // with vmcnt(0), tiles 0 and 1 included; only the workgroups whose keys
+  // reach the draft rows read them.)
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
   // the LDS mask words of wide trees are read by every wave (this barrier's
-  // wait for all memory operations costs nothing: the query loads above
+  // wait for all memory operations costs nothing: the mask loads above
   // already wait for everything in flight)
   if (tree && P.anc_words > 1) __syncthreads();
-#pragma unroll
-  for (int j = 1; j < kAhead; ++j)
-    if (j < n_tiles) issue_tile(j);
 
   // lane bases of the LDS reads (byte offsets inside a stage)
   const int k_base = (l32 >> 4) * 4096 + hf * 256 + (l32 & 15) * 16;
@@ -444,7 +475,9 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   // m_run; when the slow path moves the reference, the accumulators already
   // hold P.V of blocks up to t-1 and are rescaled with l_run, and block t's
   // probabilities (carried to step t+1 in pb_prev) use the new reference.
-  const int n_blocks = 2 * n_tiles;
+  // 32-key blocks holding keys of the slot; a slot of an odd number of
+  // blocks ends in a half tile whose second block is not computed
+  const int n_blocks = (t_end - t_begin + 31) / 32;
   const int s_mask = kStages * kStageBytes - 1;
   // stage byte offset of block tb's tile (stage sizes are a power of two)
   auto stage_of = [&](const int tb) { return lds + (((tb >> 1) * kStageBytes) & s_mask); };
@@ -531,11 +564,13 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
     step(2 * j + 1, s_b, s_a, has_pv{});
     step(2 * j + 2, s_a, s_b, has_pv{});
   }
-  step(n_blocks - 1, s_b, s_a, has_pv{});
+  // an odd block count ends inside the loop (its last step is the first
+  // block of the last tile)
+  if (!(n_blocks & 1)) step(n_blocks - 1, s_b, s_a, has_pv{});
   {
     // P.V of the last block
     bf16x8 va[4][2];
-    read_v(stage_of(n_blocks - 1), 1, va);
+    read_v(stage_of(n_blocks - 1), (n_blocks - 1) & 1, va);
     pv(va, pb_prev);
   }
 
