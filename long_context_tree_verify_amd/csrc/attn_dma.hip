@@ -132,12 +132,25 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   const int lane = tid % kWave;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  int bid = blockIdx.x;
-  const int rc = bid % P.row_chunks;
-  bid /= P.row_chunks;
+  // Workgroup -> (row chunk rc, unit = slot * B * Hkv + bg).  Consecutive
+  // workgroups go to the eight XCDs in turn, each with an L2 of its own.  The
+  // row chunks of one unit read the same K/V tiles at about the same time, so
+  // when a unit has several they go to one XCD (workgroups bid, bid + 8, ...)
+  // and all but the first find the tiles in its L2.  A unit count that is not
+  // a multiple of eight keeps the plain order.
+  const int bid = blockIdx.x;
+  int rc, unit;
+  if (P.row_chunks > 1 && (gridDim.x / P.row_chunks) % 8 == 0) {
+    const int xcd = bid % 8, k = bid / 8;
+    rc = k % P.row_chunks;
+    unit = (k / P.row_chunks) * 8 + xcd;
+  } else {
+    rc = bid % P.row_chunks;
+    unit = bid / P.row_chunks;
+  }
   const int BH = P.B * P.Hkv;
-  const int bg = bid % BH;
-  const int slot = bid / BH;
+  const int bg = unit % BH;
+  const int slot = unit / BH;
   const int b = bg / P.Hkv, g = bg % P.Hkv;
 
   // ---- key range of this slot: cache rows [t_begin, t_end) -----------------
