@@ -44,6 +44,11 @@ CASES = [
     (("ctx", (1500, 2500)), ("batch", 2), ("n_draft", 128), ("max_depth", 16)),
     (("ctx", (3000, 3000)), ("n_draft", 200), ("max_depth", 24)),
     (("ctx", (2000, 2000)), ("n_draft", 256), ("max_depth", 16)),
+    # two KV heads, two 256-row chunks per head: the automatic split count
+    # gives a multiple of eight (split, KV head) units, whose row chunks share
+    # an XCD; 1 and 7 splits give 2 and 14 units, in the plain order
+    (("ctx", (1800, 1800)), ("n_q_heads", 8), ("n_kv_heads", 2), ("n_draft", 96),
+     ("max_depth", 12)),
 ]
 
 
