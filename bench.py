@@ -332,14 +332,22 @@ def measure_paged(hsv, dev, inp, steps: int, out_dtype):
 
 
 def measure_recall(hsv, dev, steps: int):
-    """Attention recall rate of the selected index sets (Dustin page,
+    """Returns (recall, sparse_vs_dense).
+
+    recall: the attention recall rate of the selected index sets (Dustin page,
     methodology 2 names the rate; reading: the share of the full prefix's
     softmax mass the set keeps, exp(lse_set - lse_full) per query row) on
     the workload with 256 planted heavy-hitter keys per (sequence, KV head):
     importance maps that flag most of those keys -> hsv_select_kv_idx ->
     prefix-only sparse attention over the set, against prefix-only dense
     attention.  A random Zipf-ranked set of the same size is the contrast.
-    Also times the selection on these maps."""
+
+    sparse_vs_dense: whole verify steps on the same inputs (prefix or index
+    set, draft block, merge), the dense step over the full caches against the
+    sparse step over the selected sets, each K steps in a graph timed with HIP
+    events on the capture stream.  Three copies of K and V are rotated, so the
+    sparse step's gathered rows (134 MB per step) are not left in the 256 MB
+    Infinity Cache by the step before."""
     import numpy as np
     import torch
 
@@ -375,13 +383,66 @@ def measure_recall(hsv, dev, steps: int):
     torch.cuda.synchronize()
     arr = torch.exp(lse_sel.double() - lse_full.double())
     arr_rand = torch.exp(lse_rand.double() - lse_full.double())
-    return {"workload": f"{wl.name}: {wl.description}",
-            "set": f"{wl.n_sel} positions (sinks {wl.n_sink}, window {wl.n_recent}, draft top "
-                   f"{sh['n_draft_top']}) from maps flagging 70 % (draft) / 80 % (target) "
-                   f"of the planted keys",
-            "arr_mean": round(float(arr.mean()), 4), "arr_min": round(float(arr.min()), 4),
-            "arr_random_set_mean": round(float(arr_rand.mean()), 4),
-            "rows": int(arr.numel())}
+
+    copies = 3
+    ks = [k] + [k.clone() for _ in range(copies - 1)]
+    vs = [v] + [v.clone() for _ in range(copies - 1)]
+    B_, N_, Hq_, D_ = q.shape
+    o = torch.empty((B_, N_, Hq_, D_), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B_, N_, Hq_), dtype=torch.float32, device=dev)
+    desc = hsv.make_desc(batch=B_, n_draft=N_, n_q_heads=Hq_, n_kv_heads=H, head_dim=D_,
+                         kv_capacity=k.shape[2], max_ctx=max_ctx, n_sel=wl.n_sel,
+                         in_dtype=hsv.HSV_BF16, out_dtype=hsv.HSV_BF16)
+    vws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    desc.n_sel = 0
+    dws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+
+    def dense(j):
+        hsv.hsv_verify_attn(q, ks[j % copies], vs[j % copies], ctx, parent, max_ctx=max_ctx,
+                            out_dtype=torch.bfloat16, o=o, lse=lse, workspace=dws, stream=None)
+
+    def sparse(j):
+        hsv.hsv_verify_attn_sparse(q, ks[j % copies], vs[j % copies], ctx, parent, None, kv_idx,
+                                   max_ctx=max_ctx, out_dtype=torch.bfloat16, o=o, lse=lse,
+                                   workspace=vws, stream=None)
+
+    def graph_us(fn):
+        for j in range(3):
+            fn(j)
+        side = torch.cuda.Stream(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for j in range(steps):
+                fn(j)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    dense_us, sparse_us = graph_us(dense), graph_us(sparse)
+    dense_bytes = int((inp.ctx_lens.astype(np.int64) + wl.n_draft).sum()) * H * 2 * wl.head_dim * 2
+    sparse_bytes = B * H * (wl.n_sel + wl.n_draft) * 2 * wl.head_dim * 2
+    speed = {"workload": f"{wl.name}, whole verify steps (prefix or index set, draft block, "
+                         f"merge), bf16 output, {copies} cache copies rotated",
+             "dense_us_per_step": round(dense_us, 2), "sparse_us_per_step": round(sparse_us, 2),
+             "speedup": round(dense_us / sparse_us, 2),
+             "dense_kv_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+             "sparse_kv_gbs": round(sparse_bytes / (sparse_us * 1e-6) / 1e9, 1),
+             "kv_bytes_ratio": round(dense_bytes / sparse_bytes, 2)}
+    del ks, vs
+    recall = {"workload": f"{wl.name}: {wl.description}",
+              "set": f"{wl.n_sel} positions (sinks {wl.n_sink}, window {wl.n_recent}, draft "
+                     f"top {sh['n_draft_top']}) from maps flagging 70 % (draft) / 80 % "
+                     f"(target) of the planted keys",
+              "arr_mean": round(float(arr.mean()), 4), "arr_min": round(float(arr.min()), 4),
+              "arr_random_set_mean": round(float(arr_rand.mean()), 4),
+              "rows": int(arr.numel())}
+    return recall, speed
 
 
 def measure_wide_tree(hsv, dev, steps: int, out_dtype):
@@ -647,7 +708,8 @@ def main(argv=None) -> int:
     if not args.no_selection:
         log("bench: timing the index-set selection")
         result["selection"] = measure_selection(hsv, dev, args.steps, args.warmup)
-        result["selection"]["recall"] = measure_recall(hsv, dev, args.steps)
+        result["selection"]["recall"], result["sparse_vs_dense"] = measure_recall(
+            hsv, dev, args.steps)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
