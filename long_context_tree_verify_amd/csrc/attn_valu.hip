@@ -5,8 +5,10 @@
 // contiguous range of prefix keys (LongSpec section 2.C, cache part: no
 // mask) or the draft block under the ancestor mask (speculative part).
 // Per 64-key chunk: lane <-> key for the scores, then lane <-> feature for
-// P.V, with probabilities broadcast by v_readlane.  Online softmax in the
-// log2 domain; the partial is stored normalised with its natural-log LSE.
+// P.V, with probabilities broadcast by v_readlane.  Both loops have fixed trip
+// counts and no branches, so their loads are issued together rather than one
+// memory latency at a time.  Online softmax in the log2 domain; the partial
+// is stored normalised with its natural-log LSE.
 #include "common.hpp"
 #include "launch.h"
 
@@ -85,15 +87,20 @@ __global__ __launch_bounds__(256) void attn_partial_valu(Plan P) {
     } else if (valid) {
       pos = idx ? idx[t] : t;
       valid = pos >= 0 && pos < c;
-      if (!valid) pos = 0;
     }
+    // keys that take no part read row 0 of the slot (in bounds) and are
+    // dropped below; their values never reach the sums
+    if (!valid) pos = 0;
     float s = kNegInf;
-    if (valid) {
+    {
       const T *krow = kc + (kv_base + pos) * D;
+      float kr[D];
+#pragma unroll
+      for (int d = 0; d < D; ++d) kr[d] = E::load(krow, d);
       float dot = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) dot = fmaf(q_s[wave][d], E::load(krow, d), dot);
-      s = dot * P.scale_log2;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dot = fmaf(q_s[wave][d], kr[d], dot);
+      if (valid) s = dot * P.scale_log2;
     }
     const float m_new = fmaxf(m, wave_max(s));
     if (m_new == kNegInf) continue;
@@ -102,14 +109,19 @@ __global__ __launch_bounds__(256) void attn_partial_valu(Plan P) {
     l = l * alpha + wave_sum(p);
 #pragma unroll
     for (int j = 0; j < DL; ++j) acc[j] *= alpha;
-    const int n_here = min(kWave, t_end - t0);
-    for (int jj = 0; jj < n_here; ++jj) {
+    // every lane of the chunk in turn (p = 0 past the range and for dropped
+    // keys): a zero weight selects 0 instead of the row's value, so a
+    // non-finite entry of a row that takes no part cannot reach acc
+#pragma unroll 16
+    for (int jj = 0; jj < kWave; ++jj) {
       const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), jj));
-      if (pj == 0.f) continue;
       const int posj = __builtin_amdgcn_readlane(pos, jj);
       const T *vrow = vc + (kv_base + posj) * D;
 #pragma unroll
-      for (int j = 0; j < DL; ++j) acc[j] = fmaf(pj, E::load(vrow, lane + j * kWave), acc[j]);
+      for (int j = 0; j < DL; ++j) {
+        const float x = E::load(vrow, lane + j * kWave);
+        acc[j] = fmaf(pj, pj != 0.f ? x : 0.f, acc[j]);
+      }
     }
     m = m_new;
   }
