@@ -263,11 +263,23 @@ def measure_accept(hsv, dev, inp, steps: int):
 PAGED_BLOCK = 128
 
 
+def eager_us(call, steps: int) -> float:
+    """K calls issued one at a time from Python, between synchronisations."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(steps):
+        call(j)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / steps
+
+
 def measure_paged(hsv, dev, inp, steps: int, out_dtype):
     """The same verify step over a paged copy of the cache (pool blocks of
     PAGED_BLOCK tokens in seeded random order, a block table), K steps in a
-    graph with the pool copies rotated like the contiguous measurement;
-    HIP events on the capture stream bracket the replay."""
+    graph with the pool copies rotated like the contiguous measurement
+    (HIP events on the capture stream bracket the replay) and K eager calls;
+    like the contiguous step, the faster of the two is the step time."""
     import numpy as np
     import torch
 
@@ -323,11 +335,14 @@ def measure_paged(hsv, dev, inp, steps: int, out_dtype):
         g.replay()
         e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    graph_us = e0.elapsed_time(e1) * 1e3 / steps
+    eager = eager_us(call, steps)
+    us = min(graph_us, eager)
     nbytes = kv_bytes(inp)
     return {"entry": "hsv_verify_attn_paged", "block_size": bs,
             "workload": f"{wl.name}, pool blocks in random order, {copies} pool copies",
-            "us_per_step": round(us, 2), "kv_read_bytes": nbytes,
+            "us_per_step": round(us, 2), "graph_us_per_step": round(graph_us, 2),
+            "eager_us_per_step": round(eager, 2), "kv_read_bytes": nbytes,
             "achieved": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s"}
 
 
@@ -447,8 +462,8 @@ def measure_recall(hsv, dev, steps: int):
 
 def measure_wide_tree(hsv, dev, steps: int, out_dtype):
     """The 32k-context step with a 256-node draft tree (masks of four 64-bit
-    words, 1024 grouped rows per KV head): whole steps in a graph, HIP events
-    on the capture stream.  At 1024 rows the step does 4x the MFMA work per
+    words, 1024 grouped rows per KV head): whole steps in a graph (HIP events
+    on the capture stream) and K eager calls, the faster of the two.  At 1024 rows the step does 4x the MFMA work per
     KV byte of the 64-node tree, so the matrix cores bound it."""
     import numpy as np
     import torch
@@ -496,11 +511,14 @@ def measure_wide_tree(hsv, dev, steps: int, out_dtype):
         g.replay()
         e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    graph_us = e0.elapsed_time(e1) * 1e3 / steps
+    eager = eager_us(call, steps)
+    us = min(graph_us, eager)
     nbytes, flops = kv_bytes(inp), step_flops(inp)
     return {"workload": f"tree32k with a 256-node tree (depth <= 16, branching <= 4), "
                         f"{wl.group * N} grouped rows per KV head",
-            "us_per_step": round(us, 2), "kv_read_bytes": nbytes, "flop": flops,
+            "us_per_step": round(us, 2), "graph_us_per_step": round(graph_us, 2),
+            "eager_us_per_step": round(eager, 2), "kv_read_bytes": nbytes, "flop": flops,
             "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 2),
             "tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "mfma_util": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
