@@ -124,8 +124,20 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   const int cpos = SPARSE ? P.n_sel : c;
   const int lo = P.has_prefix ? 0 : cpos;
   const int hi = P.has_tree ? cpos + P.N : cpos;
-  const int t_begin = lo + slot * P.keys_per_split;
-  const int t_end = min(t_begin + P.keys_per_split, hi);
+  // Each sequence's own key range is cut into the plan's n_splits slots of
+  // equal length (rounded up to whole 32-key blocks, 64 keys for a paged
+  // cache as the plan's slots are), never longer than the plan's slot.  In a
+  // batch of unequal contexts a short sequence then has short slots instead
+  // of empty ones, so every workgroup streams and the last round of
+  // workgroups is not left to a few full-length ones.  With equal contexts
+  // the slots are the plan's.
+  const int quantum = (!SPARSE && P.block_table != nullptr) ? 64 : kBK;
+  const int len = hi - lo;
+  const int kps = min(P.keys_per_split,
+                      max(quantum, ((len + P.n_splits - 1) / P.n_splits + quantum - 1) /
+                                       quantum * quantum));
+  const int t_begin = lo + slot * kps;
+  const int t_end = min(t_begin + kps, hi);
   const int n_blocks = t_end > t_begin ? (t_end - t_begin + kBK - 1) / kBK : 0;
   const int row_last = t_end - 1;
   const bool tree = t_end > cpos;
