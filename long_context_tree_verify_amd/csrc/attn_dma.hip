@@ -30,8 +30,9 @@
 //    s_barrier, with a memory clobber so no LDS access moves across it.  No
 //    full memory fence, so later tiles stay in flight.  The query rows take
 //    the same DMA path (into two stages that tiles 2 and 3 reuse later), so
-//    the first tiles are in flight with them from the start.  M0 (the LDS base of the DMA) is
-//    set inside the same asm statement; the kernel uses M0 for nothing else.
+//    the first tiles are in flight with them from the start.  M0 (the LDS
+//    base of the DMA) is set inside the same asm statement; the kernel uses
+//    M0 for nothing else.
 //  * The V^T operands of a key block are read before its softmax, so their
 //    LDS latency overlaps the exponentials.
 //
