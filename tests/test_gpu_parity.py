@@ -252,6 +252,24 @@ def test_sparse_parity_small_poisoned(hsv, gpu, over):
     assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "sparse")
 
 
+# fp32 inputs take the vector-ALU kernel.  With no sinks, row 0 is left out of
+# almost every index set and holds NaN after poisoning; the kernel's lanes
+# past a chunk's end read row 0 and must keep it out of the scores and P.V.
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_sparse_poisoned(hsv, gpu, D):
+    over = (("ctx", (700, 700)), ("batch", 2), ("n_sel", 50), ("n_sink", 0),
+            ("n_recent", 8), ("dtype", "f32"), ("head_dim", D))
+    inp = cached_inputs("sparse64k", over, poison=True)
+    assert not inp.is_bf16 and (inp.kv_idx[..., 0] != 0).any()
+    assert np.isnan(inp.k[:, :, 0, :]).any()
+    dev = device_inputs(inp, gpu)
+    o_ref, l_ref = _oracle_all(inp)
+    for splits in (0, 3):
+        o, lse = run_hip(hsv, inp, dev, num_splits=splits)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref,
+                      f"fp32 sparse poisoned D={D} splits={splits}")
+
+
 def test_gather_kv_bit_exact(hsv, gpu):
     import torch
     inp = cached_inputs("sparse64k", SPARSE_CASES[0], poison=True)
