@@ -274,6 +274,31 @@ def eager_us(call, steps: int) -> float:
     return (time.perf_counter() - t0) * 1e6 / steps
 
 
+def measure_hbm_copy(dev, reps: int = 5):
+    """The HBM rate a plain device-to-device copy reaches in this run (1 GiB
+    read + 1 GiB written per copy, HIP events on the copy's stream): the
+    practical ceiling the step's share is also quoted against."""
+    import torch
+    n = 2 ** 28  # fp32 elements: 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    moved = 2 * n * 4
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"what": "torch device-to-device copy, 1 GiB read + 1 GiB written",
+            "bytes_moved": moved, "us": round(us, 1),
+            "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
+
+
 def measure_paged(hsv, dev, inp, steps: int, out_dtype):
     """The same verify step over a paged copy of the cache (pool blocks of
     PAGED_BLOCK tokens in seeded random order, a block table), K steps in a
@@ -715,6 +740,11 @@ def main(argv=None) -> int:
                    "graph_ms_per_step_events": round(graph_ms, 5),
                    "eager_ms_per_step": round(eager_ms, 5)},
     }
+    log("bench: timing a plain 1 GiB device copy (measured HBM ceiling)")
+    hbm = measure_hbm_copy(dev)
+    result["hbm_copy"] = hbm
+    result["pct_measured_hbm"] = round(100 * gbs / hbm["gbs"], 2)
+    result["roofline"]["frac_of_measured_copy"] = round(kern_gbs / hbm["gbs"], 4)
     if inp.kv_idx is None and bf and wl.head_dim == 128 and not args.no_paged:
         log("bench: timing the paged-cache step")
         result["paged"] = measure_paged(hsv, dev, inp, args.steps, out_dtype)
