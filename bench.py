@@ -299,6 +299,44 @@ def measure_hbm_copy(dev, reps: int = 5):
             "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
 
 
+def measure_hbm_read(dev, reps: int = 5):
+    """The HBM rate a plain read-only stream of 16-byte loads reaches in this
+    run (the probe kernel of libhsv_probe.so over 2 GiB, HIP events on its
+    stream): the measured ceiling for a kernel that mostly reads."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_tree_verify_amd", "libhsv_probe.so"))
+    lib.hsv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.hsv_probe_read.restype = ctypes.c_int
+    lib.hsv_probe_blocks.restype = ctypes.c_int
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(lib.hsv_probe_blocks(), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        rc = lib.hsv_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                ctypes.c_void_p(sink.data_ptr()),
+                                ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hsv_probe_read failed: {rc}")
+
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"what": "read-only stream of 16-byte loads (libhsv_probe), 2 GiB per pass",
+            "bytes_read": nbytes, "us": round(us, 1), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def measure_paged(hsv, dev, inp, steps: int, out_dtype):
     """The same verify step over a paged copy of the cache (pool blocks of
     PAGED_BLOCK tokens in seeded random order, a block table), K steps in a
@@ -682,6 +720,29 @@ def main(argv=None) -> int:
         part_ms.append(ek0.elapsed_time(ek1) / args.steps)
     kern_ms = sum(part_ms) / len(part_ms)
 
+    # Single steps, each between its own pair of HIP events on the stream the
+    # call runs on: the spread of the step time, and (labelled cache-assisted)
+    # the same with one cache copy reused, so the 256 MB Infinity Cache holds
+    # much of it.
+    cur = torch.cuda.current_stream(dev)
+
+    def single_steps(copy_of):
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(pairs):
+            a.record(cur)
+            call(copy_of(j))
+            b.record(cur)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+
+    def pct(xs, q):
+        return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+    flushed = single_steps(lambda j: j)
+    warm = single_steps(lambda j: 0)
+
     if args.copy_probe:
         src = torch.empty(2 ** 26, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -736,14 +797,19 @@ def main(argv=None) -> int:
                      "kernel_us_per_replay": [round(x * 1e3, 2) for x in part_ms],
                      "mfma_util": round(flops / (kern_ms * 1e-3) / 1e12 /
                                         MFMA_BF16_PEAK_TFLOPS, 4)},
+        "step_us_p10_p50_p90": [round(pct(flushed, q), 2) for q in (0.1, 0.5, 0.9)],
+        "cache_assisted_step_us_p50": round(pct(warm, 0.5), 2),
         "timing": {"graph_ms_per_step_wall": round(wall_ms, 5),
                    "graph_ms_per_step_events": round(graph_ms, 5),
                    "eager_ms_per_step": round(eager_ms, 5)},
     }
-    log("bench: timing a plain 1 GiB device copy (measured HBM ceiling)")
+    log("bench: timing a plain read-only stream and a 1 GiB copy (measured HBM ceilings)")
+    hbm_read = measure_hbm_read(dev)
     hbm = measure_hbm_copy(dev)
+    result["hbm_read"] = hbm_read
     result["hbm_copy"] = hbm
-    result["pct_measured_hbm"] = round(100 * gbs / hbm["gbs"], 2)
+    result["pct_measured_hbm"] = round(100 * gbs / hbm_read["gbs"], 2)
+    result["roofline"]["frac_of_measured_read"] = round(kern_gbs / hbm_read["gbs"], 4)
     result["roofline"]["frac_of_measured_copy"] = round(kern_gbs / hbm["gbs"], 4)
     if inp.kv_idx is None and bf and wl.head_dim == 128 and not args.no_paged:
         log("bench: timing the paged-cache step")
