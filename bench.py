@@ -138,10 +138,22 @@ def cpu_baseline(inp, target_s: float):
     gbs = kv_bytes(inp) / step_s / 1e9
     what = (f"{n} of {total}" if n < total else f"all {total}") + \
         f" (b, node, head) rows of the {wl.name} step, each over its full key set, fp64"
+    # the same oracle on one thread, over the first 8 rows of the sample
+    n1 = min(total, 8)
+    oracle.set_num_threads(1)
+    try:
+        t1 = run(n1)
+    finally:
+        oracle.set_num_threads(threads)
+    step1_s = t1 * total / n1
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{what}; {reps} run(s), {t:.2f} s measured"
                       + (f", scaled by {total}/{n}" if n < total else ""),
-            "step_s": round(step_s, 4)}
+            "step_s": round(step_s, 4),
+            "one_thread": {"value": round(kv_bytes(inp) / step1_s / 1e9, 4), "unit": "GB/s",
+                           "step_s": round(step1_s, 6),
+                           "sample": f"{n1} rows on one thread, {t1:.4f} s, scaled by "
+                                     f"{total}/{n1}"}}
 
 
 # Verification index-set selection on the sparse workload's shape: 8

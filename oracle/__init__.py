@@ -76,6 +76,8 @@ def _load():
             lib.oracle_lse_merge.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
             _lib = lib
     return _lib
 
@@ -86,6 +88,11 @@ def _ptr(a: Optional[np.ndarray]):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (timing only; results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def mask_words(n: int) -> int:

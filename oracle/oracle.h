@@ -76,6 +76,10 @@ void oracle_lse_merge(int32_t n_parts, int32_t head_dim, const double *lse_parts
 /* Number of OpenMP threads the oracle uses. */
 int oracle_num_threads(void);
 
+/* Set the number of OpenMP threads of later calls (n > 0); used to time the
+   oracle on one thread as well as on every core. */
+void oracle_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,7 @@ def test_cpu_baseline_leg():
     inp = synth.make_inputs("tiny_tree")
     r = bench.cpu_baseline(inp, 0.05)
     assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0 and r["cores"] >= 1
+    assert r["one_thread"]["value"] > 0 and r["one_thread"]["unit"] == "GB/s"
 
 
 def test_counts():
