@@ -146,7 +146,17 @@ def cpu_baseline(inp, target_s: float):
     finally:
         oracle.set_num_threads(threads)
     step1_s = t1 * total / n1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{what}; {reps} run(s), {t:.2f} s measured"
                       + (f", scaled by {total}/{n}" if n < total else ""),
             "step_s": round(step_s, 4),
