@@ -115,12 +115,15 @@ typedef struct hsv_verify_desc {
   int32_t in_dtype;    /* hsv_dtype of q, k, v                                  */
   int32_t out_dtype;   /* hsv_dtype of o                                        */
   float scale;         /* score scale; 0 means 1/sqrt(head_dim)                 */
-  int32_t num_splits;  /* key splits; 0 = automatic, else 1..256.  Dense bf16  */
-                       /* calls with D = 128 and more than 128 grouped rows    */
-                       /* (G*N) split prefix and draft rows as one range;      */
-                       /* other calls split the prefix (or index set) and add  */
-                       /* one part for the draft tree.  Results do not depend  */
-                       /* on the split count beyond rounding.                  */
+  int32_t num_splits;  /* key splits; 0 = automatic, else 1..256.  bf16 calls  */
+                       /* with D = 128 and more than 128 grouped rows (G*N,    */
+                       /* dense) or at most 32 (dense or sparse) treat the     */
+                       /* prefix (or index set) and the draft rows as one key  */
+                       /* range cut into that many slots (with at most 32      */
+                       /* rows, each sequence's range into equal slots); other */
+                       /* calls split the prefix (or index set) and add one    */
+                       /* part for the draft tree.  Results do not depend on   */
+                       /* the split count beyond rounding.                     */
   uint32_t flags;      /* HSV_FLAG_* bits                                       */
   int32_t block_size;  /* hsv_verify_attn_paged: tokens per pool block, a power */
                        /* of two >= 64 dividing kv_capacity; 0 for the other    */
