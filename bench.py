@@ -327,7 +327,11 @@ def measure_hbm_read(dev, reps: int = 5):
     stream): the measured ceiling for a kernel that mostly reads."""
     import ctypes
     import torch
-    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_tree_verify_amd", "libhsv_probe.so"))
+    path = os.path.join(ROOT, "long_context_tree_verify_amd", "libhsv_probe.so")
+    if not os.path.exists(path):
+        log(f"bench: {path} is not built; no read-only ceiling in this run")
+        return None
+    lib = ctypes.CDLL(path)
     lib.hsv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                    ctypes.c_void_p]
     lib.hsv_probe_read.restype = ctypes.c_int
@@ -830,8 +834,10 @@ def main(argv=None) -> int:
     hbm = measure_hbm_copy(dev)
     result["hbm_read"] = hbm_read
     result["hbm_copy"] = hbm
-    result["pct_measured_hbm"] = round(100 * gbs / hbm_read["gbs"], 2)
-    result["roofline"]["frac_of_measured_read"] = round(kern_gbs / hbm_read["gbs"], 4)
+    ceiling = hbm_read["gbs"] if hbm_read else hbm["gbs"]
+    result["pct_measured_hbm"] = round(100 * gbs / ceiling, 2)
+    result["roofline"]["frac_of_measured_read"] = (round(kern_gbs / hbm_read["gbs"], 4)
+                                                   if hbm_read else None)
     result["roofline"]["frac_of_measured_copy"] = round(kern_gbs / hbm["gbs"], 4)
     if inp.kv_idx is None and bf and wl.head_dim == 128 and not args.no_paged:
         log("bench: timing the paged-cache step")
