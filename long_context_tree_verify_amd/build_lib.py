@@ -19,9 +19,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libhsv.so")
-# the benchmark's read-only HBM probe, a library of its own (not part of the C ABI)
-PROBE_SRC = "hbm_probe.hip"
-PROBE_OUT = os.path.join(PKG, "libhsv_probe.so")
 BUILD = os.path.join(ROOT, "_build", "hsv")
 ARCH = "gfx950"
 
@@ -70,15 +67,8 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
-    probe_obj = _compile(PROBE_SRC)
-    tmp = PROBE_OUT + f".tmp{os.getpid()}"
-    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe_obj],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"probe link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, PROBE_OUT)
     if verbose:
-        print(f"built {OUT} and {PROBE_OUT}")
+        print(f"built {OUT}")
     return OUT
 
 

@@ -203,9 +203,13 @@ __global__ __launch_bounds__(256) void merge_verify_kernel(Plan P) {
   const int r = i * P.G + (h % P.G);
   const int64_t prow = (static_cast<int64_t>(b) * P.Hkv + g) * P.R + r;
   const int64_t stride = static_cast<int64_t>(P.B) * P.Hkv * P.R;
-  float4 acc;
-  float lse;
-  merge_row<D, F16>(P.o_part, P.lse_part, P.o_scale, P.n_parts, stride, prow, lane, &acc, &lse);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lse = kNegInf;
+  // A plan with no partials (an empty key set: no prefix keys and no tree
+  // part) has nothing to read: every row is the empty-set result.
+  if (P.n_parts > 0)
+    merge_row<D, F16>(P.o_part, P.lse_part, P.o_scale, P.n_parts, stride, prow, lane, &acc,
+                      &lse);
   store_row<D>(P.o, P.out_dtype, row * D, acc, lane);
   if (lane == 0) P.lse[row] = lse;
 }

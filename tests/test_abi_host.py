@@ -70,6 +70,16 @@ def test_workspace_size_valid_and_monotone(hsv):
     assert code == hsv.HSV_OK and t < n
 
 
+def test_empty_key_set_plan_has_no_partials(hsv):
+    """No prefix keys and no tree part: the plan holds no partial rows, so the
+    workspace is the error word alone (256 bytes) and the merge kernel must
+    not read partials (it writes o = 0, lse = -inf instead)."""
+    for kw in (dict(), dict(n_draft=8), dict(n_q_heads=16, n_draft=32, head_dim=64),
+               dict(n_q_heads=1, n_kv_heads=1, n_draft=8, head_dim=64, in_dtype=hsv.HSV_F32)):
+        code, n = _ws(hsv, _desc(hsv, max_ctx=0, flags=hsv.HSV_FLAG_NO_TREE, **kw))
+        assert code == hsv.HSV_OK and n == 256, kw
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(n_draft=0), 2), (dict(n_draft=257), 2), (dict(batch=0), 2),
     (dict(n_draft=65, head_dim=64, max_ctx=32000), 3),

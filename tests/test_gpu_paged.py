@@ -14,8 +14,7 @@ import pytest
 
 import oracle
 import synth
-from test_gpu_fullsize import sample_rows
-from util import assert_parity, cached_inputs, errors, log, to_dev
+from util import assert_all_rows, assert_parity, cached_inputs, log, oracle_full, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -103,12 +102,7 @@ def test_paged_full_size_tree32k(hsv, gpu, bs):
     inp = cached_inputs("tree32k")
     kp, vp, table = _paged(inp, bs, 99)
     o, lse = _run(hsv, gpu, inp, kp, vp, table)
-    rows = sample_rows(inp)
-    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
-                                      bf16=True, rows=rows)
-    got_o = np.stack([o[b, i, h] for b, i, h in rows])
-    got_l = np.array([lse[b, i, h] for b, i, h in rows])
-    o_err, l_err = errors(got_o, got_l, o_ref, l_ref)
-    log(f"paged tree32k bs={bs}: max|dO| = {o_err:.3e}, max rel dLSE = {l_err:.3e}")
-    assert_parity(got_o, got_l, o_ref, l_ref, f"paged tree32k bs={bs}")
+    o_ref, l_ref = oracle_full("tree32k")
+    o_err, l_err = assert_all_rows(o, lse, inp, f"paged tree32k bs={bs}", o_ref, l_ref)
+    log(f"paged tree32k bs={bs}: all rows max|dO| = {o_err:.3e}, max rel dLSE = {l_err:.3e}")
     torch.cuda.empty_cache()

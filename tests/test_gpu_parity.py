@@ -381,3 +381,35 @@ def test_graph_replays_match_eager(hsv, gpu):
             assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {rep}"
             o2, l2 = run_hip(hsv, inp, dev)      # eager work between replays
             assert torch.equal(o2, o_ref) and torch.equal(l2, l_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16_256rows", "bf16_32rows", "bf16_mfma", "f32"])
+def test_empty_key_set_without_partials(hsv, gpu, dtype):
+    """No prefix keys (max_ctx 0) and no tree part: the plan has no partial
+    results at all, and the merge writes the empty-set result (o = 0,
+    lse = -inf) without reading the workspace."""
+    import torch
+    heads = {"bf16_256rows": (32, 8, 64, 128), "bf16_32rows": (32, 8, 8, 128),
+             "bf16_mfma": (16, 8, 32, 64), "f32": (1, 1, 8, 64)}[dtype]
+    Hq, Hkv, N, D = heads
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    B, cap = 2, 64
+    q = torch.randn((B, N, Hq, D), device=gpu).to(dt)
+    k = torch.randn((B, Hkv, cap, D), device=gpu).to(dt)
+    v = torch.randn((B, Hkv, cap, D), device=gpu).to(dt)
+    ctx = torch.zeros(B, dtype=torch.int32, device=gpu)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        o = torch.full((B, N, Hq, D), float("nan"), dtype=out_dtype, device=gpu)
+        lse = torch.full((B, N, Hq), float("nan"), dtype=torch.float32, device=gpu)
+        # the smallest legal workspace for this plan (no partial rows)
+        desc = hsv.make_desc(batch=B, n_draft=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                             kv_capacity=cap, max_ctx=0,
+                             in_dtype=hsv.HSV_F32 if dt == torch.float32 else hsv.HSV_BF16,
+                             out_dtype=hsv.HSV_F32 if out_dtype == torch.float32
+                             else hsv.HSV_BF16, flags=hsv.HSV_FLAG_NO_TREE)
+        ws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=gpu)
+        hsv.hsv_verify_attn(q, k, v, ctx, None, None, max_ctx=0, out_dtype=out_dtype,
+                            flags=hsv.HSV_FLAG_NO_TREE, o=o, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        assert (o.float() == 0).all(), dtype
+        assert torch.isneginf(lse).all(), dtype

@@ -81,3 +81,36 @@ def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", o_atol=O_ATOL, lse_rt
 @functools.lru_cache(maxsize=4)
 def cached_inputs(name: str, overrides: tuple = (), poison: bool = False):
     return synth.make_inputs(name, poison_unselected=poison, **dict(overrides))
+
+
+def assert_all_rows(o_gpu, lse_gpu, inp: synth.VerifyInputs, what: str, o_ref=None, lse_ref=None,
+                    **oracle_kw):
+    """Every output row of a full-size call against the fp64 oracle, element
+    by element (the oracle runs on every host core over all B*N*Hq rows).
+    Logs the all-row maximum errors."""
+    import time
+
+    import oracle
+    if o_ref is None:
+        t = time.perf_counter()
+        kw = dict(parent=inp.parent, kv_idx=inp.kv_idx)
+        kw.update(oracle_kw)
+        o_ref, lse_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens,
+                                            bf16=inp.is_bf16, **kw)
+        log(f"  {what}: oracle over all {lse_ref.size} rows in "
+            f"{time.perf_counter() - t:.1f} s on {oracle.num_threads()} threads")
+    o_gpu = np.asarray(o_gpu)
+    lse_gpu = np.asarray(lse_gpu)
+    assert o_gpu.shape == o_ref.shape and lse_gpu.shape == lse_ref.shape
+    o_err, l_err = assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, f"{what}, all rows")
+    return o_err, l_err
+
+
+@functools.lru_cache(maxsize=2)
+def oracle_full(name: str, overrides: tuple = ()):
+    """The oracle's output over every row of a workload (cached: several
+    full-size tests share the 32k-context tree)."""
+    import oracle
+    inp = cached_inputs(name, overrides)
+    return oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                              kv_idx=inp.kv_idx, bf16=inp.is_bf16)
