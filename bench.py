@@ -9,17 +9,22 @@ Several copies of the KV cache (standing for the caches of successive
 layers) are rotated so that a step never finds its cache in the 256 MB
 Infinity Cache left over from the previous step.
 
-The K timed steps are issued two ways: one Python call per step, and replayed
-from one captured HIP graph (no host work between kernels); each is K whole
-steps between synchronisations, and the faster is the step time.
+Timing protocol (every figure on the line): W warm-up steps, then whole steps
+replayed back to back from one captured HIP graph for at least 50 ms so the
+shader clock settles at its sustained value, then EXACTLY K steps as one
+replay of the graph of K steps, between synchronisations.  ms_per_step is
+that wall time over K; HIP events on the replay's stream give the same within
+a few per cent (reported under ``timing`` with the eager per-call figure).
 
 Prints ONE JSON line (rank 0):
   value = KV-read GB/s of the whole step; ms_per_step = time per step;
   roofline = the dominant kernel (the attention partials), its average
-  duration from HIP events around five replays of a graph of K back-to-back
-  launches on its stream; traffic = its HBM bytes per launch from the committed rocprofv3
-  counter summary, when that summary was taken on the current kernel source;
-  cpu_baseline = the fp64 oracle timed on the host cores.
+  duration from HIP events around a replay of a graph of K back-to-back
+  launches on its stream (settled the same way); traffic = its HBM bytes per
+  launch from the committed rocprofv3 counter summary, when that summary was
+  taken on the current kernel source; workloads = the other four workloads'
+  whole-step figures under the same protocol; cpu_baseline = the fp64
+  oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -41,7 +46,6 @@ METRIC = "verify-step µs and KV-read GB/s (% HBM peak) at 32k ctx, 64-node tree
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 INFINITY_CACHE_BYTES = 256 * 2 ** 20
-PART_REPLAYS = 5  # timed replays of the graph of partial-kernel launches
 # Counter summary of the dominant kernel (written from rocprofv3 --pmc runs)
 # and the sources whose hash it records.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_partial_dma_tree32k_counters.md")
@@ -175,8 +179,8 @@ SELECT_SHAPE = dict(batch=8, n_kv_heads=8, score_len=65536, n_sel=4096, n_sink=4
 
 
 def measure_selection(hsv, dev, steps: int, warmup: int):
-    """Average duration of one hsv_select_kv_idx launch (HIP events around a
-    graph of `steps` launches on the stream they run on) and the algorithmic
+    """Average duration of one hsv_select_kv_idx call (the settled graph
+    protocol of `settled_timing`) and the algorithmic
     bytes it moves: each candidate score of both maps read once, the index
     set written once."""
     import numpy as np
@@ -194,22 +198,8 @@ def measure_selection(hsv, dev, steps: int, warmup: int):
     ws = torch.empty(hsv.hsv_select_workspace_bytes(B, H, L), dtype=torch.uint8, device=dev)
     kw = dict(n_sel=sh["n_sel"], n_sink=sh["n_sink"], n_recent=sh["n_recent"],
               n_draft_top=sh["n_draft_top"], kv_idx=kv_idx, workspace=ws)
-    for _ in range(warmup):
-        hsv.hsv_select_kv_idx(draft, target, ctx, **kw)
-    torch.cuda.synchronize()
-    side = torch.cuda.Stream(dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=side):
-        for _ in range(steps):
-            hsv.hsv_select_kv_idx(draft, target, ctx, **kw)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    us = settled_timing(lambda j: hsv.hsv_select_kv_idx(draft, target, ctx, **kw), steps,
+                        warmup, dev, eager=False)["us"]
     n_cand = L - sh["n_sink"] - sh["n_recent"]
     nbytes = B * H * (2 * 4 * n_cand + 4 * sh["n_sel"])
     gbs = nbytes / (us * 1e-6) / 1e9
@@ -296,6 +286,60 @@ def eager_us(call, steps: int) -> float:
     return (time.perf_counter() - t0) * 1e6 / steps
 
 
+SETTLE_MS = 50.0  # back-to-back replays before any timed region (clock settling)
+
+
+def settled_timing(call, steps: int, warmup: int, dev, settle_ms: float = SETTLE_MS,
+                   eager: bool = True):
+    """Time `call(j)` (one whole step on cache copy j) under sustained load.
+
+    W eager warm-up calls; a graph of K calls captured on a side stream;
+    replays of it back to back until at least `settle_ms` of GPU work has run
+    (the shader clock falls by 10-15 % over the first milliseconds of
+    sustained load and then holds); then ONE timed replay of the K calls,
+    between synchronisations, with HIP events on the replay's stream.
+    Returns wall and event microseconds per call (and, if asked, K eager calls
+    timed between synchronisations, for reference only)."""
+    import torch
+    for j in range(warmup):
+        call(j)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for j in range(steps):
+            call(j)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(side):
+        g.replay()
+    torch.cuda.synchronize()
+    one_ms = (time.perf_counter() - t0) * 1e3
+    # further replays back to back (no host wait between them) up to the
+    # settling time
+    n_settle = 1 + max(0, math.ceil((settle_ms - one_ms) / max(one_ms, 1e-3)))
+    with torch.cuda.stream(side):
+        for _ in range(n_settle - 1):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with torch.cuda.stream(side):
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - w0) * 1e6 / steps
+    ev_us = e0.elapsed_time(e1) * 1e3 / steps
+    out = {"us": wall_us, "event_us": ev_us, "settle_replays": n_settle,
+           "settle_ms": round((w0 - t0) * 1e3, 1)}
+    if eager:
+        out["eager_us"] = eager_us(call, steps)
+    del g
+    return out
+
+
 def measure_hbm_copy(dev, reps: int = 5):
     """The HBM rate a plain device-to-device copy reaches in this run (1 GiB
     read + 1 GiB written per copy, HIP events on the copy's stream): the
@@ -321,54 +365,11 @@ def measure_hbm_copy(dev, reps: int = 5):
             "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
 
 
-def measure_hbm_read(dev, reps: int = 5):
-    """The HBM rate a plain read-only stream of 16-byte loads reaches in this
-    run (the probe kernel of libhsv_probe.so over 2 GiB, HIP events on its
-    stream): the measured ceiling for a kernel that mostly reads."""
-    import ctypes
-    import torch
-    path = os.path.join(ROOT, "long_context_tree_verify_amd", "libhsv_probe.so")
-    if not os.path.exists(path):
-        log(f"bench: {path} is not built; no read-only ceiling in this run")
-        return None
-    lib = ctypes.CDLL(path)
-    lib.hsv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                   ctypes.c_void_p]
-    lib.hsv_probe_read.restype = ctypes.c_int
-    lib.hsv_probe_blocks.restype = ctypes.c_int
-    nbytes = 2 << 30
-    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
-    sink = torch.zeros(lib.hsv_probe_blocks(), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def launch():
-        rc = lib.hsv_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
-                                ctypes.c_void_p(sink.data_ptr()),
-                                ctypes.c_void_p(stream.cuda_stream))
-        if rc != 0:
-            raise RuntimeError(f"hsv_probe_read failed: {rc}")
-
-    launch()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        launch()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
-    del buf, sink
-    torch.cuda.empty_cache()
-    return {"what": "read-only stream of 16-byte loads (libhsv_probe), 2 GiB per pass",
-            "bytes_read": nbytes, "us": round(us, 1), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
-
-
-def measure_paged(hsv, dev, inp, steps: int, out_dtype):
+def measure_paged(hsv, dev, inp, steps: int, warmup: int, out_dtype):
     """The same verify step over a paged copy of the cache (pool blocks of
-    PAGED_BLOCK tokens in seeded random order, a block table), K steps in a
-    graph with the pool copies rotated like the contiguous measurement
-    (HIP events on the capture stream bracket the replay) and K eager calls;
-    like the contiguous step, the faster of the two is the step time."""
+    PAGED_BLOCK tokens in seeded random order, a block table), pool copies
+    rotated like the contiguous measurement, under the settled graph
+    protocol of `settled_timing`."""
     import numpy as np
     import torch
 
@@ -409,33 +410,17 @@ def measure_paged(hsv, dev, inp, steps: int, out_dtype):
                                   max_ctx=max_ctx, out_dtype=out_dtype, o=o, lse=lse,
                                   workspace=ws, stream=None)
 
-    for j in range(3):
-        call(j)
-    side = torch.cuda.Stream(dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=side):
-        for j in range(steps):
-            call(j)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(side):
-        e0.record()
-        g.replay()
-        e1.record()
-    torch.cuda.synchronize()
-    graph_us = e0.elapsed_time(e1) * 1e3 / steps
-    eager = eager_us(call, steps)
-    us = min(graph_us, eager)
+    t = settled_timing(call, steps, warmup, dev)
+    us = t["us"]
     nbytes = kv_bytes(inp)
     return {"entry": "hsv_verify_attn_paged", "block_size": bs,
             "workload": f"{wl.name}, pool blocks in random order, {copies} pool copies",
-            "us_per_step": round(us, 2), "graph_us_per_step": round(graph_us, 2),
-            "eager_us_per_step": round(eager, 2), "kv_read_bytes": nbytes,
+            "us_per_step": round(us, 2), "event_us_per_step": round(t["event_us"], 2),
+            "eager_us_per_step": round(t["eager_us"], 2), "kv_read_bytes": nbytes,
             "achieved": round(nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s"}
 
 
-def measure_recall(hsv, dev, steps: int):
+def measure_recall(hsv, dev, steps: int, warmup: int):
     """Returns (recall, sparse_vs_dense).
 
     recall: the attention recall rate of the selected index sets (Dustin page,
@@ -448,8 +433,8 @@ def measure_recall(hsv, dev, steps: int):
 
     sparse_vs_dense: whole verify steps on the same inputs (prefix or index
     set, draft block, merge), the dense step over the full caches against the
-    sparse step over the selected sets, each K steps in a graph timed with HIP
-    events on the capture stream.  Three copies of K and V are rotated, so the
+    sparse step over the selected sets, each under the settled graph protocol
+    of `settled_timing`.  Three copies of K and V are rotated, so the
     sparse step's gathered rows (134 MB per step) are not left in the 256 MB
     Infinity Cache by the step before."""
     import numpy as np
@@ -511,22 +496,7 @@ def measure_recall(hsv, dev, steps: int):
                                    workspace=vws, stream=None)
 
     def graph_us(fn):
-        for j in range(3):
-            fn(j)
-        side = torch.cuda.Stream(dev)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            for j in range(steps):
-                fn(j)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(side):
-            e0.record()
-            g.replay()
-            e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / steps
+        return settled_timing(fn, steps, warmup, dev, eager=False)["us"]
 
     dense_us, sparse_us = graph_us(dense), graph_us(sparse)
     dense_bytes = int((inp.ctx_lens.astype(np.int64) + wl.n_draft).sum()) * H * 2 * wl.head_dim * 2
@@ -549,10 +519,10 @@ def measure_recall(hsv, dev, steps: int):
     return recall, speed
 
 
-def measure_wide_tree(hsv, dev, steps: int, out_dtype):
+def measure_wide_tree(hsv, dev, steps: int, warmup: int, out_dtype):
     """The 32k-context step with a 256-node draft tree (masks of four 64-bit
-    words, 1024 grouped rows per KV head): whole steps in a graph (HIP events
-    on the capture stream) and K eager calls, the faster of the two.  At 1024 rows the step does 4x the MFMA work per
+    words, 1024 grouped rows per KV head) under the settled graph protocol
+    of `settled_timing`.  At 1024 rows the step does 4x the MFMA work per
     KV byte of the 64-node tree, so the matrix cores bound it."""
     import numpy as np
     import torch
@@ -585,70 +555,29 @@ def measure_wide_tree(hsv, dev, steps: int, out_dtype):
         hsv.hsv_verify_attn(q, ks[j % copies], vs[j % copies], ctx, parent, max_ctx=max_ctx,
                             out_dtype=out_dtype, o=o, lse=lse, workspace=ws, stream=None)
 
-    for j in range(3):
-        call(j)
-    side = torch.cuda.Stream(dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=side):
-        for j in range(steps):
-            call(j)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(side):
-        e0.record()
-        g.replay()
-        e1.record()
-    torch.cuda.synchronize()
-    graph_us = e0.elapsed_time(e1) * 1e3 / steps
-    eager = eager_us(call, steps)
-    us = min(graph_us, eager)
+    t = settled_timing(call, steps, warmup, dev)
+    us = t["us"]
     nbytes, flops = kv_bytes(inp), step_flops(inp)
     return {"workload": f"tree32k with a 256-node tree (depth <= 16, branching <= 4), "
                         f"{wl.group * N} grouped rows per KV head",
-            "us_per_step": round(us, 2), "graph_us_per_step": round(graph_us, 2),
-            "eager_us_per_step": round(eager, 2), "kv_read_bytes": nbytes, "flop": flops,
+            "us_per_step": round(us, 2), "event_us_per_step": round(t["event_us"], 2),
+            "eager_us_per_step": round(t["eager_us"], 2), "kv_read_bytes": nbytes, "flop": flops,
             "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 2),
             "tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "mfma_util": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="tree32k")
-    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-wide", action="store_true",
-                    help="skip the 256-node tree measurement")
-    ap.add_argument("--no-paged", action="store_true",
-                    help="skip the paged-cache measurement")
-    ap.add_argument("--no-selection", action="store_true",
-                    help="skip the index-set selection measurement")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 256 MiB device copy (counter calibration)")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        log("bench.py: only --gpus 1 is supported (single-GPU build; no collectives)")
-        return 2
-
+def setup_workload(hsv, dev, name: str, out_dtype, num_splits: int = 0):
+    """Inputs of one workload on the device, with enough cache copies that a
+    step never finds its K/V bytes in the Infinity Cache, and a step callable
+    call(j, flags) on copy j (torch's current stream: the capture stream
+    inside a graph)."""
     import numpy as np
     import torch
 
     import synth
-    import long_context_tree_verify_amd as hsv
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"bench: generating workload {args.workload}")
-    inp = synth.make_inputs(args.workload)
+    log(f"bench: generating workload {name}")
+    inp = synth.make_inputs(name)
     wl = inp.wl
     bf = inp.is_bf16
 
@@ -661,14 +590,14 @@ def main(argv=None) -> int:
     ctx = torch.from_numpy(inp.ctx_lens).to(dev)
     parent = torch.from_numpy(inp.parent).to(dev)
     kv_idx = None if inp.kv_idx is None else torch.from_numpy(inp.kv_idx).to(dev)
-    cache_bytes = 2 * k0.numel() * k0.element_size()
-    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / cache_bytes) + 1) if cache_bytes < \
+    # the bytes one step reads must not fit the cache twice over
+    step_bytes = kv_bytes(inp)
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / step_bytes) + 1) if step_bytes < \
         2 * INFINITY_CACHE_BYTES else 1
     ks, vs = [k0], [v0]
     for _ in range(copies - 1):
         ks.append(k0.clone())
         vs.append(v0.clone())
-    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
     B, N, Hq, D = q.shape
     o = torch.empty((B, N, Hq, D), dtype=out_dtype, device=dev)
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
@@ -678,12 +607,11 @@ def main(argv=None) -> int:
                          n_sel=0 if kv_idx is None else kv_idx.shape[2],
                          in_dtype=hsv.HSV_BF16 if bf else hsv.HSV_F32,
                          out_dtype=hsv.HSV_BF16 if out_dtype == torch.bfloat16 else hsv.HSV_F32,
-                         num_splits=args.num_splits)
+                         num_splits=num_splits)
     ws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
 
     def call(j, flags=0):
-        # stream=None: torch's current stream (the capture stream inside a graph)
-        kw = dict(max_ctx=max_ctx, out_dtype=out_dtype, num_splits=args.num_splits,
+        kw = dict(max_ctx=max_ctx, out_dtype=out_dtype, num_splits=num_splits,
                   flags=flags, o=o, lse=lse, workspace=ws, stream=None)
         c = j % copies
         if kv_idx is None:
@@ -691,60 +619,112 @@ def main(argv=None) -> int:
         else:
             hsv.hsv_verify_attn_sparse(q, ks[c], vs[c], ctx, parent, None, kv_idx, **kw)
 
-    log(f"bench: {copies} cache copies of {cache_bytes / 2**20:.1f} MiB; warmup {args.warmup}")
-    for j in range(args.warmup):
-        call(j)
-    torch.cuda.synchronize()
+    cache_bytes = 2 * k0.numel() * k0.element_size()
+    log(f"bench: {name}: {copies} cache copies of {cache_bytes / 2**20:.1f} MiB")
+    return inp, call, copies
 
-    # K steps issued one Python call at a time (reported alongside)
-    t2 = time.perf_counter()
-    for j in range(args.steps):
-        call(j)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t2) * 1e3 / args.steps
 
-    # The K timed steps as one captured graph (steps j = 0..K-1, cache copy
-    # j % copies), replayed once untimed, then once timed.
-    side = torch.cuda.Stream(dev)
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step, stream=side):
-        for j in range(args.steps):
-            call(j)
-    g_step.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    g_step.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    graph_ms = ev0.elapsed_time(ev1) / args.steps
-    # Both are whole-job times of the same K steps; report the faster issue mode.
-    ms = min(wall_ms, eager_ms)
+def kernel_name_of(inp) -> str:
+    wl = inp.wl
+    rows = wl.group * wl.n_draft
+    if not inp.is_bf16:
+        return "attn_partial_valu"
+    if inp.kv_idx is None and wl.head_dim == 128 and rows > 128:
+        return "attn_partial_dma (prefix + draft rows, split along keys)"
+    if wl.head_dim == 128 and rows <= 32:
+        return ("attn_partial_dma_small<sparse> (index set + draft rows, per-wave DMA)"
+                if inp.kv_idx is not None else
+                "attn_partial_dma_small<dense> (prefix + draft rows, per-wave DMA)")
+    return "attn_partial_mfma (prefix or index-set splits, draft slot)"
 
-    # The dominant kernel alone: K back-to-back launches of the partial phase
-    # in one graph, replayed once untimed and then PART_REPLAYS times, each
-    # replay bracketed by HIP events on the stream it runs on.  The duration
-    # is the mean over all timed launches: the chip's clock moves by about
-    # 10 % over the first few milliseconds of sustained load, so one replay
-    # alone would say more about where the clock stood than about the kernel.
-    g_part = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_part, stream=side):
-        for j in range(args.steps):
-            call(j, hsv.HSV_FLAG_PHASE_PARTIALS)
-    g_part.replay()
-    torch.cuda.synchronize()
-    part_ms = []
-    for _ in range(PART_REPLAYS):
-        ek0, ek1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ek0.record()
-        g_part.replay()
-        ek1.record()
-        torch.cuda.synchronize()
-        part_ms.append(ek0.elapsed_time(ek1) / args.steps)
-    kern_ms = sum(part_ms) / len(part_ms)
+
+def measure_step_and_kernel(hsv, call, steps: int, warmup: int, dev):
+    """Whole steps and the partial kernel alone, each under the settled
+    protocol; the kernel is a strict part of the step, so its time must not
+    exceed the step's."""
+    step = settled_timing(lambda j: call(j), steps, warmup, dev)
+    part = settled_timing(lambda j: call(j, hsv.HSV_FLAG_PHASE_PARTIALS), steps, 0, dev,
+                          eager=False)
+    return step, part
+
+
+def measure_other_workload(hsv, dev, name: str, steps: int, warmup: int, out_dtype):
+    """One of the other four workloads under the same protocol: whole-step
+    µs, its KV rate, and the share of the step the partial kernel takes."""
+    import torch
+    inp, call, copies = setup_workload(hsv, dev, name, out_dtype)
+    step, part = measure_step_and_kernel(hsv, call, steps, warmup, dev)
+    nbytes = kv_bytes(inp)
+    wl = inp.wl
+    res = {"desc": wl.description, "us_per_step": round(step["us"], 2),
+           "event_us_per_step": round(step["event_us"], 2),
+           "eager_us_per_step": round(step["eager_us"], 2),
+           "kv_read_bytes": nbytes, "flop": step_flops(inp),
+           "kv_gbs": round(nbytes / (step["us"] * 1e-6) / 1e9, 1),
+           "pct_hbm_peak": round(100 * nbytes / (step["us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+           "kernel": kernel_name_of(inp), "kernel_us": round(part["event_us"], 2),
+           "kernel_gbs": round(nbytes / (part["event_us"] * 1e-6) / 1e9, 1),
+           "kernel_share_of_step": round(part["event_us"] / step["us"], 4),
+           "cache_copies": copies, "steps": steps}
+    if part["event_us"] > step["us"] * 1.02:
+        raise AssertionError(f"{name}: partial kernel {part['event_us']:.2f} us exceeds the "
+                             f"step {step['us']:.2f} us")
+    del call
+    torch.cuda.empty_cache()
+    return res
+
+
+OTHER_WORKLOADS = ("tiny_tree", "chain_b16", "tree128k", "sparse64k")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="tree32k")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-wide", action="store_true",
+                    help="skip the 256-node tree measurement")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-cache measurement")
+    ap.add_argument("--no-selection", action="store_true",
+                    help="skip the index-set selection measurement")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other four workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py: only --gpus 1 is supported (single-GPU build; no collectives)")
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        log("bench.py: --steps must be >= 1 and --warmup >= 0")
+        return 2
+
+    import torch
+
+    import long_context_tree_verify_amd as hsv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    inp, call, copies = setup_workload(hsv, dev, args.workload, out_dtype, args.num_splits)
+    wl = inp.wl
+    bf = inp.is_bf16
+    max_ctx = int(inp.ctx_lens.max())
+
+    log(f"bench: {args.workload}: warm-up {args.warmup}, settle >= {SETTLE_MS:.0f} ms, "
+        f"then {args.steps} timed steps")
+    step, part = measure_step_and_kernel(hsv, call, args.steps, args.warmup, dev)
+    us = step["us"]
+    kern_us = part["event_us"]
 
     # Single steps, each between its own pair of HIP events on the stream the
     # call runs on: the spread of the step time, and (labelled cache-assisted)
@@ -778,20 +758,12 @@ def main(argv=None) -> int:
 
     nbytes = kv_bytes(inp)
     flops = step_flops(inp)
-    traffic = recorded_traffic(wl.name) if kv_idx is None and bf else None
-    rows = wl.group * wl.n_draft
-    if not bf:
-        kernel_name = "attn_partial_valu"
-    elif kv_idx is None and wl.head_dim == 128 and rows > 128:
-        kernel_name = "attn_partial_dma (prefix + draft rows, split along keys)"
-    elif wl.head_dim == 128 and rows <= 32:
-        kernel_name = ("attn_partial_dma_small<sparse> (index set + draft rows, per-wave DMA)"
-                       if kv_idx is not None else
-                       "attn_partial_dma_small<dense> (prefix + draft rows, per-wave DMA)")
-    else:
-        kernel_name = "attn_partial_mfma (prefix or index-set splits, draft slot)"
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    kern_gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(wl.name) if inp.kv_idx is None and bf else None
+    gbs = nbytes / (us * 1e-6) / 1e9
+    kern_gbs = nbytes / (kern_us * 1e-6) / 1e9
+    if kern_us > us * 1.02:
+        raise AssertionError(f"partial kernel {kern_us:.2f} us exceeds the whole step "
+                             f"{us:.2f} us: the timing is not steady")
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -799,8 +771,8 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "us_per_step": round(ms * 1e3, 2),
+        "ms_per_step": round(us * 1e-3, 5),
+        "us_per_step": round(us, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -818,40 +790,60 @@ def main(argv=None) -> int:
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)",
                      "algorithmic_bytes_per_launch": nbytes,
-                     "kernel": kernel_name,
-                     "kernel_us": round(kern_ms * 1e3, 2),
-                     "kernel_us_per_replay": [round(x * 1e3, 2) for x in part_ms],
-                     "mfma_util": round(flops / (kern_ms * 1e-3) / 1e12 /
+                     "kernel": kernel_name_of(inp),
+                     "kernel_us": round(kern_us, 2),
+                     "kernel_share_of_step": round(kern_us / us, 4),
+                     "mfma_util": round(flops / (kern_us * 1e-6) / 1e12 /
                                         MFMA_BF16_PEAK_TFLOPS, 4)},
         "step_us_p10_p50_p90": [round(pct(flushed, q), 2) for q in (0.1, 0.5, 0.9)],
         "cache_assisted_step_us_p50": round(pct(warm, 0.5), 2),
-        "timing": {"graph_ms_per_step_wall": round(wall_ms, 5),
-                   "graph_ms_per_step_events": round(graph_ms, 5),
-                   "eager_ms_per_step": round(eager_ms, 5)},
+        "timing": {"protocol": f"{args.warmup} warm-up steps, graph replays of "
+                               f"{args.steps} steps back to back for >= {SETTLE_MS:.0f} ms "
+                               f"({step['settle_replays']} replays, {step['settle_ms']} ms), "
+                               f"then one timed replay of {args.steps} steps between "
+                               f"synchronisations",
+                   "wall_us_per_step": round(us, 2),
+                   "event_us_per_step": round(step["event_us"], 2),
+                   "eager_us_per_step": round(step["eager_us"], 2),
+                   "kernel_settle_replays": part["settle_replays"]},
     }
-    log("bench: timing a plain read-only stream and a 1 GiB copy (measured HBM ceilings)")
-    hbm_read = measure_hbm_read(dev)
+    del call
+    torch.cuda.empty_cache()
+    log("bench: timing a 1 GiB device copy (a plain stream for comparison)")
     hbm = measure_hbm_copy(dev)
-    result["hbm_read"] = hbm_read
     result["hbm_copy"] = hbm
-    ceiling = hbm_read["gbs"] if hbm_read else hbm["gbs"]
-    result["pct_measured_hbm"] = round(100 * gbs / ceiling, 2)
-    result["roofline"]["frac_of_measured_read"] = (round(kern_gbs / hbm_read["gbs"], 4)
-                                                   if hbm_read else None)
-    result["roofline"]["frac_of_measured_copy"] = round(kern_gbs / hbm["gbs"], 4)
+    streams = {"hbm_copy": hbm["gbs"], f"{wl.name}_step": gbs, f"{wl.name}_kernel": kern_gbs}
+    if wl.name == "tree32k" and not args.no_others:
+        result["workloads"] = {}
+        for other in OTHER_WORKLOADS:
+            log(f"bench: timing workload {other}")
+            res = measure_other_workload(hsv, dev, other, min(args.steps, 200),
+                                         args.warmup, out_dtype)
+            result["workloads"][other] = res
+            if other != "tiny_tree":
+                streams[f"{other}_step"] = res["kv_gbs"]
+                streams[f"{other}_kernel"] = res["kernel_gbs"]
     if inp.kv_idx is None and bf and wl.head_dim == 128 and not args.no_paged:
         log("bench: timing the paged-cache step")
-        result["paged"] = measure_paged(hsv, dev, inp, args.steps, out_dtype)
+        result["paged"] = measure_paged(hsv, dev, inp, args.steps, args.warmup, out_dtype)
     if wl.name == "tree32k" and not args.no_wide:
         log("bench: timing the 256-node tree step")
-        result["wide_tree"] = measure_wide_tree(hsv, dev, args.steps, out_dtype)
+        result["wide_tree"] = measure_wide_tree(hsv, dev, min(args.steps, 100), args.warmup,
+                                                out_dtype)
     log("bench: timing the accepted-path cache update")
     result["accept"] = measure_accept(hsv, dev, inp, args.steps)
     if not args.no_selection:
         log("bench: timing the index-set selection")
         result["selection"] = measure_selection(hsv, dev, args.steps, args.warmup)
         result["selection"]["recall"], result["sparse_vs_dense"] = measure_recall(
-            hsv, dev, args.steps)
+            hsv, dev, min(args.steps, 100), args.warmup)
+        streams["sparse_vs_dense_dense_step"] = result["sparse_vs_dense"]["dense_kv_gbs"]
+    # The fastest stream this run reached (a plain copy, or any step or
+    # kernel above): the measured ceiling the step's rate is also quoted
+    # against.
+    best = max(streams, key=streams.get)
+    result["best_stream"] = {"what": best, "gbs": round(streams[best], 1)}
+    result["pct_best_stream"] = round(100 * gbs / streams[best], 2)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
