@@ -4,10 +4,12 @@
  * C ABI.  Every pointer argument is a device pointer unless stated
  * otherwise; every buffer belongs to the caller.  The library allocates and
  * frees no device memory: scratch lives in the caller's workspace, sized by
- * hsv_verify_workspace_bytes().  Work is enqueued on `stream` and the calls
+ * hsv_verify_workspace_bytes() (hsv_verify_attn_noalloc: a static array the
+ * library's code object holds on each GPU).  Work is enqueued on `stream` and the calls
  * return without synchronising the host (except under HSV_FLAG_VALIDATE).
  * The library keeps no mutable global state, so concurrent calls on different
- * streams with different workspaces are safe.
+ * streams with different workspaces are safe -- except hsv_verify_attn_noalloc,
+ * whose scratch is one library-owned array per GPU (see there).
  *
  * What is computed.  LongSpec ("Long-Context Lossless Speculative Decoding
  * with Efficient Drafting and Verification"), section 2.C "Hybrid Tree
@@ -277,6 +279,30 @@ hsv_status hsv_lse_merge(const float *o_parts, const float *lse_parts,
                          int32_t n_parts, int64_t n_rows, int32_t head_dim,
                          void *o, float *lse, int32_t out_dtype,
                          hipStream_t stream);
+
+/* Size of the scratch array hsv_verify_attn_noalloc uses on each GPU. */
+#define HSV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* hsv_verify_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same computation, arguments, kernels
+ * and results as hsv_verify_attn; the scratch those kernels use is a
+ * library-owned device array of HSV_NOALLOC_SCRATCH_BYTES on each GPU, held
+ * from the first call on that GPU until the process ends.  No device memory
+ * is allocated or freed by the call.  A descriptor whose workspace
+ * (hsv_verify_workspace_bytes) exceeds HSV_NOALLOC_SCRATCH_BYTES returns
+ * HSV_ERR_WORKSPACE; a paged (block_size != 0) or sparse (n_sel != 0)
+ * descriptor returns HSV_ERR_SHAPE.  Every call on one GPU shares that GPU's
+ * array and it keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that overlap on one GPU (different streams, or
+ * different host threads without ordering) race and give wrong results.
+ * The GPU is the device of `stream` (the current device for the null
+ * stream). */
+hsv_status hsv_verify_attn_noalloc(const hsv_verify_desc *d, const void *q,
+                                   const void *k_cache, const void *v_cache,
+                                   const int32_t *ctx_lens, const int32_t *parent,
+                                   const uint64_t *anc_mask, void *o, float *lse,
+                                   hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *hsv_status_string(hsv_status s);

@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     HSV_FLAG_PHASE_MERGE,
     HSV_FLAG_PHASE_PARTIALS,
     HSV_FLAG_VALIDATE,
+    HSV_NOALLOC_SCRATCH_BYTES,
     HSV_OK,
     HsvError,
     HsvVerifyDesc,
@@ -165,6 +166,40 @@ def hsv_verify_attn_sparse(q, k_cache, v_cache, ctx_lens, parent=None, anc_mask=
     return _verify(True, q, k_cache, v_cache, ctx_lens, parent, anc_mask, kv_idx,
                    max_ctx=max_ctx, out_dtype=out_dtype, scale=scale, num_splits=num_splits,
                    flags=flags, o=o, lse=lse, workspace=workspace, stream=stream)
+
+
+def hsv_verify_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            ctx_lens: torch.Tensor, parent: Optional[torch.Tensor] = None,
+                            anc_mask: Optional[torch.Tensor] = None, *, max_ctx: int,
+                            o: torch.Tensor, lse: torch.Tensor, scale: float = 0.0,
+                            num_splits: int = 0, flags: int = 0, stream=None) -> None:
+    """hsv_verify_attn with the library's own per-GPU scratch instead of a
+    workspace (see include/hsv.h).  Allocates nothing: the caller passes o
+    [B, N, Hq, D] (float32 or bfloat16) and lse float32 [B, N, Hq]."""
+    B, N, Hq, D = q.shape
+    Bk, Hkv, cap, Dk = k_cache.shape
+    if (Bk, Dk) != (B, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    in_dt = _dtype_code(q, "q")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("ctx_lens must be int32 [B]")
+    if parent is not None and (parent.dtype != torch.int32 or tuple(parent.shape) != (B, N)):
+        raise ValueError("parent must be int32 [B, N]")
+    _check_mask(anc_mask, B, N)
+    out_dt = _dtype_code(o, "o")
+    if tuple(o.shape) != (B, N, Hq, D) or lse.dtype != torch.float32 or \
+            tuple(lse.shape) != (B, N, Hq):
+        raise ValueError("o must be [B, N, Hq, D] and lse float32 [B, N, Hq]")
+    desc = make_desc(batch=B, n_draft=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                     kv_capacity=cap, max_ctx=int(max_ctx), in_dtype=in_dt, out_dtype=out_dt,
+                     scale=scale, num_splits=num_splits, flags=flags)
+    _check_dev(q, k_cache, v_cache, ctx_lens, parent, anc_mask, o, lse)
+    _check(lib.hsv_verify_attn_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(ctx_lens), _ptr(parent),
+                                       _ptr(anc_mask), _ptr(o), _ptr(lse),
+                                       _stream(stream, q.device)), "hsv_verify_attn_noalloc")
 
 
 def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

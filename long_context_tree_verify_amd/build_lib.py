@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build", "hsv")
 ARCH = "gfx950"
 
 SOURCES = ["hsv_api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_dma.hip", "attn_dma_small.hip", "aux_kernels.hip",
-           "select.hip", "kv_update.hip"]
+           "select.hip", "kv_update.hip", "noalloc.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
