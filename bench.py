@@ -340,6 +340,86 @@ def settled_timing(call, steps: int, warmup: int, dev, settle_ms: float = SETTLE
     return out
 
 
+def _smi_sample():
+    """(socket power W, mean gfx clock MHz) from amd-smi, or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=10)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r'"socket_power": \{\s*"value": (\d+)', r.stdout)
+    c = re.findall(r'"gfx_\d+": \{\s*"clk": \{\s*"value": (\d+)', r.stdout)
+    if not m:
+        return None
+    return int(m.group(1)), (sum(int(x) for x in c) / len(c) if c else None)
+
+
+def idle_power():
+    """Mean socket power over a second with the GPU idle (taken before any
+    work in the process), or None."""
+    xs = []
+    for _ in range(10):
+        x = _smi_sample()
+        if x:
+            xs.append(x[0])
+        time.sleep(0.1)
+    return sum(xs) / len(xs) if xs else None
+
+
+def measure_power(call, steps: int, dev, p_idle, seconds: float = 2.0):
+    """Socket power and shader clock (amd-smi, sampled from a second thread)
+    while `call` replays back to back from a graph of `steps` calls for
+    `seconds`, against the idle reading just before.  The energy per call is
+    (power - idle) x the call's duration in that run.  None if amd-smi gives
+    no reading."""
+    import threading
+    import torch
+    if p_idle is None:
+        return None
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for j in range(steps):
+            call(j)
+    torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            x = _smi_sample()
+            if x:
+                samples.append(x)
+            time.sleep(0.05)
+
+    th = threading.Thread(target=poll)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        with torch.cuda.stream(side):
+            for _ in range(5):
+                g.replay()
+        torch.cuda.synchronize()
+        n += 5
+    dt = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    del g
+    steady = samples[len(samples) // 3:]
+    if not steady:
+        return None
+    p = sum(x for x, _ in steady) / len(steady)
+    clk = [c for _, c in steady if c]
+    us = dt * 1e6 / (n * steps)
+    return {"socket_w": round(p, 1), "idle_w": round(p_idle, 1),
+            "gfx_mhz": round(sum(clk) / len(clk)) if clk else None,
+            "us_per_call": round(us, 2),
+            "dynamic_mj_per_call": round((p - p_idle) * us * 1e-3, 2),
+            "samples": len(steady), "seconds": round(dt, 2)}
+
+
 def measure_hbm_copy(dev, reps: int = 5):
     """The HBM rate a plain device-to-device copy reaches in this run (1 GiB
     read + 1 GiB written per copy, HIP events on the copy's stream): the
@@ -712,6 +792,7 @@ def main(argv=None) -> int:
 
     import long_context_tree_verify_amd as hsv
 
+    p_idle = idle_power()  # before this process puts any load on the GPU
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
@@ -807,6 +888,9 @@ def main(argv=None) -> int:
                    "eager_us_per_step": round(step["eager_us"], 2),
                    "kernel_settle_replays": part["settle_replays"]},
     }
+    log("bench: socket power and shader clock under back-to-back partial-kernel launches")
+    result["roofline"]["power"] = measure_power(
+        lambda j: call(j, hsv.HSV_FLAG_PHASE_PARTIALS), args.steps, dev, p_idle)
     del call
     torch.cuda.empty_cache()
     log("bench: timing a 1 GiB device copy (a plain stream for comparison)")
