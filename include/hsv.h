@@ -103,9 +103,7 @@ typedef enum hsv_dtype { HSV_F32 = 0, HSV_BF16 = 1 } hsv_dtype;
 
 typedef struct hsv_verify_desc {
   int32_t batch;       /* B >= 1                                                */
-  int32_t n_draft;     /* N in [1, 256]; above 64 only where the call uses the  */
-                       /* 256-row kernel (bf16, D = 128, more than 128        */
-                       /* grouped rows), else HSV_ERR_UNSUPPORTED             */
+  int32_t n_draft;     /* N in [1, 256] (above 64, masks of ceil(N/64) words)   */
   int32_t n_q_heads;   /* Hq >= 1, a multiple of n_kv_heads                     */
   int32_t n_kv_heads;  /* Hkv >= 1                                              */
   int32_t head_dim;    /* D: 64 or 128                                          */
@@ -211,7 +209,7 @@ hsv_status hsv_gather_kv(const void *k_cache, const void *v_cache,
  * ctx_lens[b] + depth(i) - 1, where a child of the prefix (parent -1) has
  * depth 1 -- the position node i would take if its branch were accepted, as
  * a rotary embedding needs it.  parent [B, N] int32 in [-1, i-1]; ctx_lens
- * [B] int32; pos_ids [B, N] int32 out.  N in [1, 64].  Every entry of a
+ * [B] int32; pos_ids [B, N] int32 out.  N in [1, 256].  Every entry of a
  * sequence with an out-of-range parent is written as -1. */
 hsv_status hsv_tree_position_ids(const int32_t *parent, const int32_t *ctx_lens,
                                  int32_t *pos_ids, int32_t batch, int32_t n_draft,
@@ -229,7 +227,7 @@ hsv_status hsv_tree_position_ids(const int32_t *parent, const int32_t *ctx_lens,
  * accepts nothing.  A sequence with accept_node outside [-1, N), an
  * out-of-range parent, c_b < 0 or c_b + N > S_cap is left unchanged.
  * ctx_lens is read and updated on the device (stream-ordered: two
- * launches); parent [B, N] and accept_node [B] are int32.  N in [1, 64]. */
+ * launches); parent [B, N] and accept_node [B] are int32.  N in [1, 256]. */
 hsv_status hsv_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens,
                            const int32_t *parent, const int32_t *accept_node,
                            int32_t batch, int32_t n_kv_heads, int32_t kv_capacity,

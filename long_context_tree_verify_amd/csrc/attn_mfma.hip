@@ -275,7 +275,10 @@ __global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
     }
     anc_q[qb] = 0;
     if (tree) {
-      if (P.anc)
+      if (P.anc_words > 1)  // trees of more than 64 nodes: the row's mask words
+        anc_q[qb] = reinterpret_cast<uintptr_t>(P.anc + (static_cast<int64_t>(b) * P.N + i) *
+                                                           P.anc_words);
+      else if (P.anc)
         anc_q[qb] = P.anc[static_cast<int64_t>(b) * P.N + i];
       else
         anc_q[qb] = shfl_u64(anc_lane, i);
@@ -364,8 +367,19 @@ __global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
         for (int qb = 0; qb < C::QB; ++qb) {
           uint32_t keep = lim;
           if (tree) {
-            const int sh = kb0 + 4 * hf;
-            keep &= sh < 64 ? static_cast<uint32_t>(anc_q[qb] >> sh) : 0u;
+            // draft node of the block's first key: tile base plus block offset
+            const int kt = t0 + kb0;
+            const int sh = kt + 4 * hf;
+            if (P.anc_words > 1) {
+              // the 32-bit chunk kt / 32 of the row's mask (kt is a multiple
+              // of 32 and the lane's keys lie in [kt, kt + 32)); anc_q holds
+              // the address of the row's words
+              const uint32_t *a32 = reinterpret_cast<const uint32_t *>(anc_q[qb]);
+              const int ch = kt >> 5;
+              keep &= ch < 2 * P.anc_words ? a32[ch] >> (4 * hf) : 0u;
+            } else {
+              keep &= sh < 64 ? static_cast<uint32_t>(anc_q[qb] >> sh) : 0u;
+            }
           }
 #pragma unroll
           for (int e = 0; e < 16; ++e) {

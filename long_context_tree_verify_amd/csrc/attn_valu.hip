@@ -55,7 +55,9 @@ __global__ __launch_bounds__(256) void attn_partial_valu(Plan P) {
   if (tree) {
     t_begin = 0;
     t_end = P.N;
-    if (P.anc) {
+    if (P.anc_words > 1) {
+      anc_i = 0;  // trees of more than 64 nodes: one mask word per 64-key chunk below
+    } else if (P.anc) {
       anc_i = P.anc[static_cast<int64_t>(b) * P.N + i];
     } else {
       bool bad;
@@ -83,7 +85,12 @@ __global__ __launch_bounds__(256) void attn_partial_valu(Plan P) {
     int pos = 0;
     if (tree) {
       pos = c + t;
-      valid = valid && ((anc_i >> (t & 63)) & 1u);
+      // word t0 / 64 of the row's mask (wave-uniform: t0 is a multiple of 64)
+      const uint64_t word = P.anc_words > 1
+                                ? P.anc[(static_cast<int64_t>(b) * P.N + i) * P.anc_words +
+                                        min(t0 >> 6, P.anc_words - 1)]
+                                : anc_i;
+      valid = valid && ((word >> (t & 63)) & 1u);
     } else if (valid) {
       pos = idx ? idx[t] : t;
       valid = pos >= 0 && pos < c;

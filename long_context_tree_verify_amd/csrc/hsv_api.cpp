@@ -130,8 +130,6 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
   p->unified = p->kernel == kKernDma256 || p->kernel == kKernDmaSmall;
   const bool paged = d->block_size > 0;
   if (paged && !p->unified) return HSV_ERR_UNSUPPORTED;
-  // trees of more than 64 nodes: the 256-row kernel only (multi-word masks)
-  if (p->N > 64 && with_tree && p->kernel != kKernDma256) return HSV_ERR_UNSUPPORTED;
   if (p->unified) {
     // One key range per (b, kv head): prefix (or index set) then draft rows.  One workgroup
     // per CU: as many splits as fit in one round of the CUs (splits of a
@@ -403,7 +401,7 @@ hsv_status hsv_tree_position_ids(const int32_t *parent, const int32_t *ctx_lens,
                                  int32_t *pos_ids, int32_t batch, int32_t n_draft,
                                  hipStream_t stream) {
   if (!parent || !ctx_lens || !pos_ids) return HSV_ERR_NULL;
-  if (batch < 1 || n_draft < 1 || n_draft > 64) return HSV_ERR_SHAPE;
+  if (batch < 1 || n_draft < 1 || n_draft > kMaxDraft) return HSV_ERR_SHAPE;
   return launch_tree_position_ids(parent, ctx_lens, pos_ids, batch, n_draft, stream) == hipSuccess
              ? HSV_OK
              : HSV_ERR_HIP;
@@ -416,7 +414,7 @@ hsv_status hsv_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens, cons
   if (!k_cache || !v_cache || !ctx_lens || !parent || !accept_node) return HSV_ERR_NULL;
   if (dtype != HSV_F32 && dtype != HSV_BF16) return HSV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return HSV_ERR_UNSUPPORTED;
-  if (batch < 1 || n_kv_heads < 1 || n_draft < 1 || n_draft > 64 || kv_capacity < n_draft)
+  if (batch < 1 || n_kv_heads < 1 || n_draft < 1 || n_draft > kMaxDraft || kv_capacity < n_draft)
     return HSV_ERR_SHAPE;
   if (static_cast<int64_t>(batch) * n_kv_heads > (int64_t{1} << 31) - 1) return HSV_ERR_SHAPE;
   const int row_bytes = head_dim * (dtype == HSV_F32 ? 4 : 2);

@@ -82,8 +82,9 @@ def test_empty_key_set_plan_has_no_partials(hsv):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n_draft=0), 2), (dict(n_draft=257), 2), (dict(batch=0), 2),
-    (dict(n_draft=65, head_dim=64, max_ctx=32000), 3),
-    (dict(n_draft=65, n_q_heads=8, max_ctx=32000), 3), (dict(n_draft=256, max_ctx=32000), 0),
+    (dict(n_draft=65, head_dim=64, max_ctx=32000), 0),
+    (dict(n_draft=65, n_q_heads=8, max_ctx=32000), 0), (dict(n_draft=256, max_ctx=32000), 0),
+    (dict(n_draft=200, n_q_heads=8, head_dim=64, max_ctx=32000, in_dtype=0), 0),
     (dict(n_q_heads=30), 2), (dict(n_kv_heads=0), 2), (dict(head_dim=96), 3),
     (dict(max_ctx=32769), 2), (dict(max_ctx=-1), 2), (dict(num_splits=257), 2),
     (dict(num_splits=-1), 2), (dict(in_dtype=7), 3), (dict(out_dtype=2), 3),

@@ -37,7 +37,7 @@ def _trees(rng, B, N):
 def test_position_ids(hsv, gpu):
     import torch
     rng = np.random.Generator(np.random.PCG64(61))
-    for N in (1, 2, 7, 33, 64):
+    for N in (1, 2, 7, 33, 64, 65, 130, 256):
         par = _trees(rng, 12, N)
         if N > 1:
             par[5, N - 1] = N - 1          # self-parent: the sequence is invalid
@@ -45,7 +45,7 @@ def test_position_ids(hsv, gpu):
         got = hsv.hsv_tree_position_ids(torch.from_numpy(par).to(gpu),
                                         torch.from_numpy(ctx).to(gpu)).cpu().numpy()
         np.testing.assert_array_equal(got, oracle.tree_position_ids(par, ctx))
-    log("  position ids identical for N in 1, 2, 7, 33, 64")
+    log("  position ids identical for N in 1, 2, 7, 33, 64, 65, 130, 256")
 
 
 def _bits(t):
@@ -128,3 +128,24 @@ def test_accept_full_size(hsv, gpu, name):
     k = rng.integers(0, 1 << 16, n, dtype=np.uint16).reshape(B, H, S, D)
     v = rng.integers(0, 1 << 16, n, dtype=np.uint16).reshape(B, H, S, D)
     _check_accept(hsv, gpu, k, v, ctx, par, node, True, f"{name} shape")
+
+
+@pytest.mark.parametrize("bf16,D,N", [(True, 128, 256), (False, 128, 200), (True, 64, 97)])
+def test_accept_wide_trees(hsv, gpu, bf16, D, N):
+    """Trees of more than 64 nodes: chains (the longest paths, moved in
+    several staged chunks), deep random trees and the deepest node."""
+    rng = np.random.Generator(np.random.PCG64(65 + N))
+    B, H, S = 8, 3, N + 500
+    par = np.stack([synth.chain_parents(N), np.full(N, -1, np.int32),
+                    synth.uniform_parents(rng, N),
+                    synth.random_tree_parents(rng, N, max_depth=N, max_branch=2),
+                    synth.random_tree_parents(rng, N, max_depth=16, max_branch=4),
+                    synth.chain_parents(N), synth.uniform_parents(rng, N),
+                    synth.random_tree_parents(rng, N, max_depth=N, max_branch=1)]
+                   ).astype(np.int32)
+    ctx = rng.integers(0, S - N + 1, B).astype(np.int32)
+    depth = oracle.tree_depth(par)
+    node = depth.argmax(axis=1)
+    node[1], node[6] = -1, rng.integers(0, N)
+    k, v = _cache(rng, B, H, S, D, bf16)
+    _check_accept(hsv, gpu, k, v, ctx, par, node, bf16, f"N={N} trees bf16={bf16} D={D}")

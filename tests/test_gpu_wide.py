@@ -117,9 +117,43 @@ def test_wide_tree_full_size(hsv, gpu):
         f"max rel dLSE = {l_err:.3e}")
 
 
-def test_wide_tree_unsupported_shapes(hsv, gpu):
-    inp = cached_inputs("tree32k", (("ctx", (500, 500)), ("n_draft", 80), ("head_dim", 64),
-                                    ("max_depth", 12)))
+# Trees of more than 64 nodes on the kernels other than the 256-row DMA one:
+# the MFMA kernels (D = 64, or 33 to 128 grouped rows) read a 32-bit chunk of
+# the row's mask words per key block, the fp32 kernel one word per 64 keys.
+OTHER_KERNEL_CASES = [
+    ("tree32k", (("ctx", (500, 500)), ("n_draft", 80), ("head_dim", 64), ("max_depth", 12))),
+    ("tree32k", (("ctx", (700, 900)), ("batch", 2), ("n_draft", 100), ("n_q_heads", 8),
+                 ("n_kv_heads", 8), ("max_depth", 20))),
+    ("tree32k", (("ctx", (600, 600)), ("n_draft", 200), ("n_q_heads", 8), ("n_kv_heads", 8),
+                 ("head_dim", 64), ("max_depth", 24))),
+    ("tree32k", (("ctx", (400, 400)), ("n_draft", 120), ("n_q_heads", 2), ("n_kv_heads", 2),
+                 ("max_depth", 16))),
+    ("tiny_tree", (("ctx", (300, 300)), ("n_draft", 96))),
+    ("tiny_tree", (("ctx", (200, 200)), ("n_draft", 256), ("head_dim", 128))),
+]
+
+
+@pytest.mark.parametrize("case", range(len(OTHER_KERNEL_CASES)))
+def test_wide_tree_other_kernels(hsv, gpu, case):
+    import torch
+    name, over = OTHER_KERNEL_CASES[case]
+    inp = cached_inputs(name, over)
     dev = device_inputs(inp, gpu)
-    with pytest.raises(RuntimeError, match="UNSUPPORTED"):
-        run_hip(hsv, inp, dev)
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                                      bf16=inp.is_bf16)
+    what = f"{name} {dict(over)}"
+    for splits in (0, 3):
+        o, lse = run_hip(hsv, inp, dev, num_splits=splits)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"{what} splits={splits}")
+    anc = oracle.ancestor_mask(inp.parent)
+    o, lse = run_hip(hsv, inp, dev, parent=None,
+                     anc=torch.from_numpy(np.ascontiguousarray(anc).view(np.int64)).to(gpu))
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"{what} mask words")
+    # block-parallel masks (bits above the row's own index)
+    N = inp.wl.n_draft
+    blk = np.broadcast_to(synth.block_masks(N, 40), (inp.wl.batch,) + synth.block_masks(N, 40).shape)
+    blk = np.ascontiguousarray(blk)
+    o, lse = run_hip(hsv, inp, dev, parent=None,
+                     anc=torch.from_numpy(blk.view(np.int64)).to(gpu))
+    ob, lb = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, anc_mask=blk, bf16=inp.is_bf16)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), ob, lb, f"{what} blocks of 40")
