@@ -275,8 +275,10 @@ __global__ __launch_bounds__(256) void validate_kernel(Plan P) {
     for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
       const int s = static_cast<int>(e % P.n_sel);
       const int32_t *row = P.kv_idx + static_cast<int64_t>(b) * n + (e - s);
+      // a strictly increasing run of positions in [0, c), then -1 slots
       const int t = row[s];
-      if (t < 0 || t >= c || (s > 0 && row[s - 1] >= t)) bits |= kErrIndex;
+      if (t != -1 && (t < 0 || t >= c || (s > 0 && (row[s - 1] >= t || row[s - 1] == -1))))
+        bits |= kErrIndex;
     }
   }
   if (P.block_table && c >= 0 && static_cast<int64_t>(c) + P.N <= P.cap) {

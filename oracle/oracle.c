@@ -94,8 +94,12 @@ static void attend_row(const oracle_desc *d, const void *q, const void *k,
   memset(mask, 0, (size_t)span);
   if (d->parts & ORACLE_PART_PREFIX) {
     if (d->n_sel > 0) {
+      /* Dustin page, methodology 1: a fixed-size verification set; when the
+       * history is shorter than the set, the set is all of it and the slots
+       * left over hold -1 (no position). */
       const int32_t *idx = kv_idx + ((int64_t)b * Hkv + g) * d->n_sel;
-      for (int32_t s = 0; s < d->n_sel; ++s) mask[idx[s]] = 1;
+      for (int32_t s = 0; s < d->n_sel; ++s)
+        if (idx[s] >= 0) mask[idx[s]] = 1;
     } else {
       for (int64_t t = 0; t < c; ++t) mask[t] = 1;
     }
@@ -168,8 +172,11 @@ int oracle_verify_attn(const oracle_desc *d, const void *q, const void *k,
       }
     if (d->n_sel > 0)
       for (int64_t s = 0; s < (int64_t)d->n_kv_heads * d->n_sel; ++s) {
-        int32_t t = kv_idx[(int64_t)b * d->n_kv_heads * d->n_sel + s];
-        if (t < 0 || t >= ctx_lens[b]) return -1;
+        const int32_t *row = kv_idx + (int64_t)b * d->n_kv_heads * d->n_sel;
+        int32_t t = row[s];
+        /* a position in [0, c_b), or -1 in a tail of -1 entries */
+        if (t < -1 || t >= ctx_lens[b]) return -1;
+        if (s % d->n_sel > 0 && row[s - 1] == -1 && t != -1) return -1;
       }
   }
   const int64_t total = rows ? n_rows : (int64_t)d->batch * d->n_draft * d->n_q_heads;

@@ -15,7 +15,8 @@
  *   for each sequence b, draft node i, query head h, with g = h / (Hq/Hkv):
  *     A = P(b,g) u { c_b + j : j in T(b,i) }        (explicit 0/1 mask row)
  *       P(b,g) = [0, c_b)                 dense
- *              = { kv_idx[b,g,k] }        sparse
+ *              = { kv_idx[b,g,k] : kv_idx[b,g,k] >= 0 }   sparse (-1: empty slot,
+ *                                                  only in a tail of -1 entries)
  *       T(b,i) = { i, parent[i], parent[parent[i]], ... }   (walk until -1)
  *                or the set bits of anc_mask[b,i,:] when given instead
  *     s_t = scale * sum_d q[b,i,h,d] * k[b,g,t,d]          (fp64)

@@ -211,3 +211,35 @@ def test_recall_rate_parity(hsv, gpu):
         f"max rel diff {rel.max():.2e}, random set {np.exp(l_rand - l_full).mean():.4f}")
     assert (rel <= bound).all()
     assert arr_gpu.mean() > 2.0 * np.exp(l_rand - l_full).mean()
+
+
+def test_select_then_sparse_verify_short_histories(hsv, gpu):
+    """The selection's -1 tail (histories shorter than the set) is a valid
+    sparse index set: the sparse call accepts it under HSV_FLAG_VALIDATE and
+    matches the oracle on the same set (which, for those sequences, is the
+    whole history: dense attention)."""
+    import torch
+    inp = synth.make_inputs("chain_b16", ctx=(200, 1500), batch=6)
+    B, Hkv, cap = inp.k.shape[:3]
+    ctx = inp.ctx_lens
+    assert (ctx < 512).any() and (ctx > 512).any()
+    rng = np.random.Generator(np.random.PCG64(509))
+    draft, target = synth.importance_maps(rng, ctx, Hkv, int(ctx.max()))
+    kw = dict(n_sel=512, n_sink=4, n_recent=64, n_draft_top=200)
+    idx = _select(hsv, gpu, draft, target, ctx, **kw)
+    np.testing.assert_array_equal(idx, oracle.select_kv_idx(draft, target, ctx, **kw))
+    assert (idx == -1).any()
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(gpu)
+    o, lse = hsv.hsv_verify_attn_sparse(
+        up(inp.q), up(inp.k), up(inp.v), torch.from_numpy(ctx).to(gpu),
+        torch.from_numpy(inp.parent).to(gpu), None, torch.from_numpy(idx).to(gpu),
+        max_ctx=int(ctx.max()), flags=hsv.HSV_FLAG_VALIDATE)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, ctx, parent=inp.parent, kv_idx=idx,
+                                      bf16=True)
+    from util import assert_parity
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "select -> sparse verify")
+    short = ctx < 512
+    dense_ref = oracle.verify_attn(inp.q[short], inp.k[short], inp.v[short], ctx[short],
+                                   parent=inp.parent[short], bf16=True)
+    np.testing.assert_allclose(o_ref[short], dense_ref[0], rtol=0, atol=1e-12)

@@ -414,6 +414,33 @@ def test_sparse_all_indices_equals_dense():
     np.testing.assert_allclose(sparse[1], dense[1], rtol=0, atol=1e-12)
 
 
+def test_sparse_set_with_empty_slots_equals_dense():
+    """A set that holds the whole history followed by -1 slots (what the
+    selection writes when the history is shorter than the set) attends to
+    exactly the dense prefix; a -1 before a position is rejected."""
+    inp = synth.make_inputs("sparse64k", ctx=(300, 300), n_sel=300, n_recent=32, batch=2,
+                            n_q_heads=4, n_kv_heads=2, head_dim=32)
+    c = 300
+    assert (inp.kv_idx == np.arange(c)).all()
+    padded = np.concatenate([inp.kv_idx, np.full(inp.kv_idx.shape[:2] + (57,), -1, np.int32)],
+                            axis=2)
+    dense = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent, bf16=True)
+    sparse = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                                kv_idx=padded, bf16=True)
+    np.testing.assert_allclose(sparse[0], dense[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sparse[1], dense[1], rtol=0, atol=1e-12)
+    bad = padded.copy()
+    bad[1, 0, c + 3] = 5                  # a position after a -1 slot
+    with pytest.raises(ValueError):
+        oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent, kv_idx=bad,
+                           bf16=True)
+    bad = padded.copy()
+    bad[0, 1, 7] = -2
+    with pytest.raises(ValueError):
+        oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent, kv_idx=bad,
+                           bf16=True)
+
+
 def test_sparse_equals_dense_over_gathered_cache_and_ignores_poison():
     kw = dict(ctx=(1500, 1500), n_sel=300, n_recent=64, batch=2, n_q_heads=4, n_kv_heads=2,
               head_dim=32)
