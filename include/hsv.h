@@ -49,7 +49,9 @@
  *   anc_mask [B, N, W]           uint64, W = ceil(N / 64) words per node;
  *                                bit j % 64 of word j / 64 = node j visible
  *                                from node i ([B, N] when N <= 64)
- *   kv_idx   [B, Hkv, n_sel]     int32, strictly increasing, each < c_b
+ *   kv_idx   [B, Hkv, n_sel]     int32: strictly increasing positions < c_b,
+ *                                optionally followed by -1 entries (empty
+ *                                slots of a set larger than the history)
  *   o        [B, N, Hq, D]       out_dtype
  *   lse      [B, N, Hq]          float
  *
@@ -100,6 +102,14 @@ typedef enum hsv_dtype { HSV_F32 = 0, HSV_BF16 = 1 } hsv_dtype;
  * phases.  Lets a caller time the phases apart or place work between them. */
 #define HSV_FLAG_PHASE_PARTIALS 8u
 #define HSV_FLAG_PHASE_MERGE 16u
+/* Keep the split partials in fp32.  By default the bf16, D = 128 kernels
+ * with more than 128 or at most 32 grouped rows store each normalised
+ * partial row as fp16 times a power of two (the row's largest |value| in
+ * [0.5, 1), 11 significant bits per value, half the workspace and traffic
+ * of fp32); the other kernels always use fp32.  The flag doubles the
+ * partials' bytes; it serves to measure what the fp16 storage costs in
+ * accuracy, which stays within 2^-11 of the largest |o| of a row per split. */
+#define HSV_FLAG_F32_PARTIALS 32u
 
 typedef struct hsv_verify_desc {
   int32_t batch;       /* B >= 1                                                */
@@ -147,8 +157,10 @@ hsv_status hsv_verify_attn(const hsv_verify_desc *d, const void *q,
                            void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* Sparse verification attention: prefix = the d->n_sel cache positions in
- * kv_idx[b, g, :] (strictly increasing, each < c_b), plus the draft tree.
+/* Sparse verification attention: prefix = the cache positions in
+ * kv_idx[b, g, :] (strictly increasing, each < c_b; a tail of -1 entries
+ * marks empty slots, as hsv_select_kv_idx writes when c_b < n_sel), plus the
+ * draft tree.
  * Same arguments and rules as hsv_verify_attn otherwise. */
 hsv_status hsv_verify_attn_sparse(const hsv_verify_desc *d, const void *q,
                                   const void *k_cache, const void *v_cache,

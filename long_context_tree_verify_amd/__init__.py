@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     HSV_ERR_UNSUPPORTED,
     HSV_ERR_WORKSPACE,
     HSV_F32,
+    HSV_FLAG_F32_PARTIALS,
     HSV_FLAG_NO_PREFIX,
     HSV_FLAG_NO_TREE,
     HSV_FLAG_PHASE_MERGE,

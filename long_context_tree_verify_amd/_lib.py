@@ -26,6 +26,7 @@ HSV_FLAG_NO_PREFIX = 2
 HSV_FLAG_NO_TREE = 4
 HSV_FLAG_PHASE_PARTIALS = 8
 HSV_FLAG_PHASE_MERGE = 16
+HSV_FLAG_F32_PARTIALS = 32
 
 HSV_NOALLOC_SCRATCH_BYTES = 32 << 20
 

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   if (n_tiles == 0) {
     if (r < P.R && hf == 0) {
       P.lse_part[prow] = kNegInf;
-      P.o_scale[prow] = 1.f;
+      if (P.part_f16) P.o_scale[prow] = 1.f;
     }
     return;
   }
@@ -609,7 +609,24 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
   const float mul = ldexpf(inv, -ex);
   if (hf == 0 && r < P.R) {
     P.lse_part[prow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
-    P.o_scale[prow] = ldexpf(1.f, ex);
+    if (P.part_f16) P.o_scale[prow] = ldexpf(1.f, ex);
+  }
+  if (!P.part_f16) {
+    // fp32 partial rows (HSV_FLAG_F32_PARTIALS) straight from the
+    // accumulators: each lane stores four consecutive features at a time
+    if (r < P.R) {
+      float *dst = P.o_part + prow * kD + 4 * hf;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          floatx4 v4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v4[q] = o_acc[db][4 * jj + q] * inv;
+          *reinterpret_cast<floatx4 *>(dst + 32 * db + 8 * jj) = v4;
+        }
+    }
+    return;
   }
   __syncthreads();  // every wave is done with the K/V stages
   char *ep = smem + wave * 32 * kEpiRowStride;
@@ -638,7 +655,8 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma(Plan P) {
 
 }  // namespace
 
-// The kernel writes its partials in the scaled fp16 format (part_f16).
+// The kernel writes its partials in the scaled fp16 format (part_f16), or in
+// fp32 when the caller asks for it.
 bool dma_supports(const Plan &p) {
   return p.in_dtype == kBF16 && p.D == kD && p.n_sel == 0 && p.R > 128;
 }

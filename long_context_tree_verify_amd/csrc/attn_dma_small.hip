@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   if (n_blocks == 0) {
     if (wave == 0 && hf == 0 && r < P.R) {
       P.lse_part[prow] = kNegInf;
-      P.o_scale[prow] = 1.f;
+      if (P.part_f16) P.o_scale[prow] = 1.f;
     }
     return;
   }
@@ -502,6 +502,19 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     const float *src = reinterpret_cast<const float *>(smem + (w * kRows + row) * kEpiRow) + f0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) o16[e] = fmaf(wt, src[e], o16[e]);
+  }
+  if (!P.part_f16) {
+    // fp32 partial rows (HSV_FLAG_F32_PARTIALS)
+    if (row < P.R) {
+      const int64_t orow = (static_cast<int64_t>(slot) * BH + bg) * P.R + row;
+      float *dst = P.o_part + orow * kD + f0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4)
+        *reinterpret_cast<float4 *>(dst + e) = make_float4(o16[e], o16[e + 1], o16[e + 2],
+                                                           o16[e + 3]);
+      if ((tid & 7) == 0) P.lse_part[orow] = L > 0.f ? (M + fast_log2(L)) * kLn2 : kNegInf;
+    }
+    return;
   }
   // scaled fp16: the row's largest |value| in [0.5, 1), scale to o_scale
   float amax = 0.f;

@@ -41,7 +41,8 @@ hsv_status check_desc(const hsv_verify_desc *d, bool sparse) {
   if (d->num_splits < 0 || d->num_splits > kMaxSplits) return HSV_ERR_SHAPE;
   if (!(d->scale >= 0.f) || isinf(d->scale)) return HSV_ERR_SHAPE;
   const uint32_t known = HSV_FLAG_VALIDATE | HSV_FLAG_NO_PREFIX | HSV_FLAG_NO_TREE |
-                         HSV_FLAG_PHASE_PARTIALS | HSV_FLAG_PHASE_MERGE;
+                         HSV_FLAG_PHASE_PARTIALS | HSV_FLAG_PHASE_MERGE |
+                         HSV_FLAG_F32_PARTIALS;
   if (d->flags & ~known) return HSV_ERR_UNSUPPORTED;
   if ((d->flags & HSV_FLAG_NO_PREFIX) && (d->flags & HSV_FLAG_NO_TREE)) return HSV_ERR_SHAPE;
   if (sparse) {
@@ -162,7 +163,7 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
     p->tree_slot = -1;
     p->n_slots = p->n_splits;
     p->n_parts = p->n_slots * p->kgroups;
-    p->part_f16 = 1;
+    p->part_f16 = (d->flags & HSV_FLAG_F32_PARTIALS) ? 0 : 1;
     *ws_bytes = workspace_bytes(*p);
     return HSV_OK;
   }

@@ -89,7 +89,8 @@ def test_empty_key_set_plan_has_no_partials(hsv):
     (dict(max_ctx=32769), 2), (dict(max_ctx=-1), 2), (dict(num_splits=257), 2),
     (dict(num_splits=-1), 2), (dict(in_dtype=7), 3), (dict(out_dtype=2), 3),
     (dict(scale=-1.0), 2), (dict(scale=float("nan")), 2), (dict(flags=64), 3),
-    (dict(flags=6), 2), (dict(n_sel=5000, max_ctx=4000), 2), (dict(flags=32), 3),
+    (dict(flags=6), 2), (dict(n_sel=5000, max_ctx=4000), 2), (dict(flags=128), 3),
+    (dict(flags=32), 0),
 ])
 def test_workspace_rejects_bad_descriptors(hsv, kw, code):
     got, _ = _ws(hsv, _desc(hsv, **kw))

@@ -413,3 +413,29 @@ def test_empty_key_set_without_partials(hsv, gpu, dtype):
         torch.cuda.synchronize()
         assert (o.float() == 0).all(), dtype
         assert torch.isneginf(lse).all(), dtype
+
+
+@pytest.mark.parametrize("wl", ["tree32k", "chain_b16", "sparse64k"])
+def test_f32_partials_small(hsv, gpu, wl):
+    """HSV_FLAG_F32_PARTIALS on both DMA kernels (256-row and small-group,
+    dense and gathered): parity against the oracle for several split counts,
+    and the two phases run apart give the combined call's result bit for
+    bit."""
+    import torch
+    over = {"tree32k": (("ctx", (3000, 3000)),),
+            "chain_b16": (("ctx", (500, 2100)), ("batch", 4)),
+            "sparse64k": SPARSE_CASES[1]}[wl]
+    inp = cached_inputs(wl, over, poison=wl == "sparse64k")
+    dev = device_inputs(inp, gpu)
+    o_ref, l_ref = _oracle_all(inp)
+    F = hsv.HSV_FLAG_F32_PARTIALS
+    for splits in (0, 1, 7):
+        o, lse = run_hip(hsv, inp, dev, num_splits=splits, flags=F)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref,
+                      f"{wl} fp32 partials splits={splits}")
+    o, lse = run_hip(hsv, inp, dev, flags=F)
+    o2, l2 = torch.empty_like(o), torch.empty_like(lse)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=gpu)
+    run_hip(hsv, inp, dev, flags=F | hsv.HSV_FLAG_PHASE_PARTIALS, o=o2, lse=l2, workspace=ws)
+    run_hip(hsv, inp, dev, flags=F | hsv.HSV_FLAG_PHASE_MERGE, o=o2, lse=l2, workspace=ws)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
