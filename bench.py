@@ -32,6 +32,7 @@ Prints ONE JSON line (rank 0):
 from __future__ import annotations
 
 import argparse
+import functools
 import json
 import math
 import os
@@ -446,10 +447,11 @@ def measure_hbm_copy(dev, reps: int = 5):
 
 
 def measure_paged(hsv, dev, inp, steps: int, warmup: int, out_dtype):
-    """The same verify step over a paged copy of the cache (pool blocks of
-    PAGED_BLOCK tokens in seeded random order, a block table), pool copies
-    rotated like the contiguous measurement, under the settled graph
-    protocol of `settled_timing`."""
+    """The same verify step (dense, or sparse over the workload's index sets)
+    over a paged copy of the cache (pool blocks of PAGED_BLOCK tokens in
+    seeded random order, a block table), pool copies rotated like the
+    contiguous measurement, under the settled graph protocol of
+    `settled_timing`."""
     import numpy as np
     import torch
 
@@ -466,8 +468,9 @@ def measure_paged(hsv, dev, inp, steps: int, warmup: int, out_dtype):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
     k0, v0 = up(kp), up(vp)
-    pool_bytes = 2 * k0.numel() * k0.element_size()
-    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / pool_bytes) + 1) if pool_bytes < \
+    # the bytes one step reads (a sparse step reads only its index sets' rows)
+    step_bytes = kv_bytes(inp)
+    copies = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / step_bytes) + 1) if step_bytes < \
         2 * INFINITY_CACHE_BYTES else 1
     ks, vs = [k0] + [k0.clone() for _ in range(copies - 1)], [v0] + [v0.clone()
                                                                       for _ in range(copies - 1)]
@@ -475,25 +478,33 @@ def measure_paged(hsv, dev, inp, steps: int, warmup: int, out_dtype):
     tab = torch.from_numpy(table).to(dev)
     ctx = torch.from_numpy(inp.ctx_lens).to(dev)
     parent = torch.from_numpy(inp.parent).to(dev)
+    kv_idx = None if inp.kv_idx is None else torch.from_numpy(inp.kv_idx).to(dev)
     B, N, Hq, D = q.shape
     o = torch.empty((B, N, Hq, D), dtype=out_dtype, device=dev)
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
     max_ctx = int(inp.ctx_lens.max())
     desc = hsv.make_desc(batch=B, n_draft=N, n_q_heads=Hq, n_kv_heads=wl.n_kv_heads,
-                         head_dim=D, kv_capacity=cap, max_ctx=max_ctx, in_dtype=hsv.HSV_BF16,
+                         head_dim=D, kv_capacity=cap, max_ctx=max_ctx,
+                         n_sel=0 if kv_idx is None else kv_idx.shape[2], in_dtype=hsv.HSV_BF16,
                          out_dtype=hsv.HSV_BF16 if out_dtype == torch.bfloat16 else hsv.HSV_F32,
                          block_size=bs)
     ws = torch.empty(hsv.hsv_verify_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kw = dict(max_ctx=max_ctx, out_dtype=out_dtype, o=o, lse=lse, workspace=ws, stream=None)
+    entry = "hsv_verify_attn_paged" if kv_idx is None else "hsv_verify_attn_sparse_paged"
 
     def call(j):
-        hsv.hsv_verify_attn_paged(q, ks[j % copies], vs[j % copies], tab, ctx, parent,
-                                  max_ctx=max_ctx, out_dtype=out_dtype, o=o, lse=lse,
-                                  workspace=ws, stream=None)
+        if kv_idx is None:
+            hsv.hsv_verify_attn_paged(q, ks[j % copies], vs[j % copies], tab, ctx, parent, **kw)
+        else:
+            hsv.hsv_verify_attn_sparse_paged(q, ks[j % copies], vs[j % copies], tab, ctx,
+                                             parent, None, kv_idx, **kw)
 
     t = settled_timing(call, steps, warmup, dev)
     us = t["us"]
-    nbytes = kv_bytes(inp)
-    return {"entry": "hsv_verify_attn_paged", "block_size": bs,
+    nbytes = step_bytes
+    del ks, vs, k0, v0
+    torch.cuda.empty_cache()
+    return {"entry": entry, "block_size": bs,
             "workload": f"{wl.name}, pool blocks in random order, {copies} pool copies",
             "us_per_step": round(us, 2), "event_us_per_step": round(t["event_us"], 2),
             "eager_us_per_step": round(t["eager_us"], 2), "kv_read_bytes": nbytes,
@@ -647,6 +658,15 @@ def measure_wide_tree(hsv, dev, steps: int, warmup: int, out_dtype):
             "mfma_util": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+@functools.lru_cache(maxsize=2)
+def workload_inputs(name: str):
+    """The seeded host inputs of a workload (kept: the paged measurement
+    reuses the 64k sparse workload's)."""
+    import synth
+    log(f"bench: generating workload {name}")
+    return synth.make_inputs(name)
+
+
 def setup_workload(hsv, dev, name: str, out_dtype, num_splits: int = 0):
     """Inputs of one workload on the device, with enough cache copies that a
     step never finds its K/V bytes in the Infinity Cache, and a step callable
@@ -655,9 +675,7 @@ def setup_workload(hsv, dev, name: str, out_dtype, num_splits: int = 0):
     import numpy as np
     import torch
 
-    import synth
-    log(f"bench: generating workload {name}")
-    inp = synth.make_inputs(name)
+    inp = workload_inputs(name)
     wl = inp.wl
     bf = inp.is_bf16
 
@@ -910,6 +928,10 @@ def main(argv=None) -> int:
     if inp.kv_idx is None and bf and wl.head_dim == 128 and not args.no_paged:
         log("bench: timing the paged-cache step")
         result["paged"] = measure_paged(hsv, dev, inp, args.steps, args.warmup, out_dtype)
+    if wl.name == "tree32k" and not args.no_paged and not args.no_others:
+        log("bench: timing the paged sparse step (sparse64k)")
+        result["paged_sparse"] = measure_paged(hsv, dev, workload_inputs("sparse64k"),
+                                               min(args.steps, 200), args.warmup, out_dtype)
     if wl.name == "tree32k" and not args.no_wide:
         log("bench: timing the 256-node tree step")
         result["wide_tree"] = measure_wide_tree(hsv, dev, min(args.steps, 100), args.warmup,

@@ -135,7 +135,7 @@ typedef struct hsv_verify_desc {
                        /* part for the draft tree.  Results do not depend on   */
                        /* the split count beyond rounding.                     */
   uint32_t flags;      /* HSV_FLAG_* bits                                       */
-  int32_t block_size;  /* hsv_verify_attn_paged: tokens per pool block, a power */
+  int32_t block_size;  /* paged calls: tokens per pool block, a power         */
                        /* of two >= 64 dividing kv_capacity; 0 for the other    */
                        /* calls                                                 */
 } hsv_verify_desc;
@@ -194,6 +194,28 @@ hsv_status hsv_verify_attn_paged(const hsv_verify_desc *d, const void *q,
                                  const uint64_t *anc_mask, void *o, float *lse,
                                  void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/* Sparse verification attention over a paged cache (Dustin page: the
+ * verification attends to a selected subset of a fully indexed cache;
+ * HiSpec page: that cache paged with block tables).  Same computation as
+ * hsv_verify_attn_sparse on the cache that the pool and table describe as in
+ * hsv_verify_attn_paged: kv_idx[b, g, :] holds logical positions (strictly
+ * increasing, each < c_b, then an optional tail of -1 slots) and each
+ * selected row, like each draft row c_b + j, is read from the pool block its
+ * table entry names.  Runs where the contiguous sparse call uses the
+ * small-group DMA kernel (bf16, D = 128, at most 32 grouped rows) and the
+ * table has at most 6144 columns (kv_capacity / block_size); other shapes
+ * and HSV_FLAG_NO_PREFIX return HSV_ERR_UNSUPPORTED.  Table entries outside
+ * the pool are clamped into it (wrong values, no read outside the pool;
+ * HSV_FLAG_VALIDATE reports them).  The pool may exceed 4 GiB.  Workspace
+ * size from hsv_verify_workspace_bytes with the same descriptor. */
+hsv_status hsv_verify_attn_sparse_paged(const hsv_verify_desc *d, const void *q,
+                                        const void *k_pool, const void *v_pool,
+                                        const int32_t *block_table, int32_t n_pool_blocks,
+                                        const int32_t *ctx_lens, const int32_t *parent,
+                                        const uint64_t *anc_mask, const int32_t *kv_idx, void *o,
+                                        float *lse, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
 
 /* Ancestor bitmask of each draft tree (LongSpec section 2.C: the mask of the
  * speculative part follows the branches of the tree).

@@ -203,16 +203,9 @@ def hsv_verify_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                                        _stream(stream, q.device)), "hsv_verify_attn_noalloc")
 
 
-def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-                          block_table: torch.Tensor, ctx_lens: torch.Tensor,
-                          parent: Optional[torch.Tensor] = None,
-                          anc_mask: Optional[torch.Tensor] = None, *, max_ctx: int,
-                          out_dtype=torch.float32, scale: float = 0.0, num_splits: int = 0,
-                          flags: int = 0, o=None, lse=None, workspace=None, stream=None
-                          ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Dense verification attention over a paged cache (see include/hsv.h):
-    k_pool, v_pool [n_blocks, Hkv, block_size, D]; block_table int32
-    [B, max_blocks].  Returns (o, lse)."""
+def _verify_paged(sparse: bool, q, k_pool, v_pool, block_table, ctx_lens, parent, anc_mask,
+                  kv_idx, *, max_ctx, out_dtype, scale, num_splits, flags, o, lse, workspace,
+                  stream):
     B, N, Hq, D = q.shape
     n_pool, Hkv, bs, Dk = k_pool.shape
     if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape):
@@ -227,6 +220,12 @@ def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
     if parent is not None and (parent.dtype != torch.int32 or tuple(parent.shape) != (B, N)):
         raise ValueError("parent must be int32 [B, N]")
     _check_mask(anc_mask, B, N)
+    n_sel = 0
+    if sparse:
+        if kv_idx is None or kv_idx.dtype != torch.int32 or kv_idx.dim() != 3 or \
+                tuple(kv_idx.shape[:2]) != (B, Hkv):
+            raise ValueError("kv_idx must be int32 [B, Hkv, n_sel]")
+        n_sel = kv_idx.shape[2]
     if o is None:
         o = torch.empty((B, N, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None:
@@ -236,19 +235,54 @@ def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
             tuple(lse.shape) != (B, N, Hq):
         raise ValueError("o must be [B, N, Hq, D] and lse float32 [B, N, Hq]")
     desc = make_desc(batch=B, n_draft=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
-                     kv_capacity=block_table.shape[1] * bs, max_ctx=int(max_ctx), in_dtype=in_dt,
-                     out_dtype=out_dt, scale=scale, num_splits=num_splits, flags=flags,
-                     block_size=bs)
+                     kv_capacity=block_table.shape[1] * bs, max_ctx=int(max_ctx), n_sel=n_sel,
+                     in_dtype=in_dt, out_dtype=out_dt, scale=scale, num_splits=num_splits,
+                     flags=flags, block_size=bs)
     need = hsv_verify_workspace_bytes(desc)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check_dev(q, k_pool, v_pool, block_table, ctx_lens, parent, anc_mask, o, lse, workspace)
-    _check(lib.hsv_verify_attn_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-                                     _ptr(block_table), n_pool, _ptr(ctx_lens), _ptr(parent),
-                                     _ptr(anc_mask), _ptr(o), _ptr(lse), _ptr(workspace),
-                                     ctypes.c_size_t(workspace.numel()),
-                                     _stream(stream, q.device)), "hsv_verify_attn_paged")
+    _check_dev(q, k_pool, v_pool, block_table, ctx_lens, parent, anc_mask, kv_idx, o, lse,
+               workspace)
+    head = (ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), n_pool,
+            _ptr(ctx_lens), _ptr(parent), _ptr(anc_mask))
+    tail = (_ptr(o), _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+            _stream(stream, q.device))
+    if sparse:
+        _check(lib.hsv_verify_attn_sparse_paged(*head, _ptr(kv_idx), *tail),
+               "hsv_verify_attn_sparse_paged")
+    else:
+        _check(lib.hsv_verify_attn_paged(*head, *tail), "hsv_verify_attn_paged")
     return o, lse
+
+
+def hsv_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                          block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                          parent: Optional[torch.Tensor] = None,
+                          anc_mask: Optional[torch.Tensor] = None, *, max_ctx: int,
+                          out_dtype=torch.float32, scale: float = 0.0, num_splits: int = 0,
+                          flags: int = 0, o=None, lse=None, workspace=None, stream=None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Dense verification attention over a paged cache (see include/hsv.h):
+    k_pool, v_pool [n_blocks, Hkv, block_size, D]; block_table int32
+    [B, max_blocks].  Returns (o, lse)."""
+    return _verify_paged(False, q, k_pool, v_pool, block_table, ctx_lens, parent, anc_mask,
+                         None, max_ctx=max_ctx, out_dtype=out_dtype, scale=scale,
+                         num_splits=num_splits, flags=flags, o=o, lse=lse,
+                         workspace=workspace, stream=stream)
+
+
+def hsv_verify_attn_sparse_paged(q, k_pool, v_pool, block_table, ctx_lens, parent=None,
+                                 anc_mask=None, kv_idx=None, *, max_ctx: int,
+                                 out_dtype=torch.float32, scale: float = 0.0,
+                                 num_splits: int = 0, flags: int = 0, o=None, lse=None,
+                                 workspace=None, stream=None):
+    """Sparse verification attention over a paged cache (see include/hsv.h):
+    the pool and table as in hsv_verify_attn_paged, kv_idx int32
+    [B, Hkv, n_sel] of logical positions.  Returns (o, lse)."""
+    return _verify_paged(True, q, k_pool, v_pool, block_table, ctx_lens, parent, anc_mask,
+                         kv_idx, max_ctx=max_ctx, out_dtype=out_dtype, scale=scale,
+                         num_splits=num_splits, flags=flags, o=o, lse=lse,
+                         workspace=workspace, stream=stream)
 
 
 def hsv_tree_ancestor_mask(parent: torch.Tensor, anc_mask: Optional[torch.Tensor] = None,

@@ -36,6 +36,7 @@ EXPORTS = (
     "hsv_verify_attn",
     "hsv_verify_attn_sparse",
     "hsv_verify_attn_paged",
+    "hsv_verify_attn_sparse_paged",
     "hsv_verify_attn_noalloc",
     "hsv_tree_ancestor_mask",
     "hsv_gather_kv",
@@ -87,6 +88,7 @@ def load() -> ctypes.CDLL:
     lib.hsv_verify_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, sz, P]
     lib.hsv_verify_attn_sparse.argtypes = [D, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.hsv_verify_attn_paged.argtypes = [D, P, P, P, P, i32, P, P, P, P, P, P, sz, P]
+    lib.hsv_verify_attn_sparse_paged.argtypes = [D, P, P, P, P, i32, P, P, P, P, P, P, P, sz, P]
     lib.hsv_verify_attn_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P]
     lib.hsv_tree_ancestor_mask.argtypes = [P, P, i32, i32, P]
     lib.hsv_gather_kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
@@ -96,7 +98,9 @@ def load() -> ctypes.CDLL:
     lib.hsv_tree_position_ids.argtypes = [P, P, P, i32, i32, P]
     lib.hsv_accept_path.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     for name in ("hsv_verify_workspace_bytes", "hsv_verify_attn", "hsv_verify_attn_sparse",
-                 "hsv_verify_attn_paged", "hsv_verify_attn_noalloc", "hsv_tree_ancestor_mask", "hsv_gather_kv", "hsv_lse_merge",
+                 "hsv_verify_attn_paged", "hsv_verify_attn_sparse_paged",
+                 "hsv_verify_attn_noalloc", "hsv_tree_ancestor_mask", "hsv_gather_kv",
+                 "hsv_lse_merge",
                  "hsv_select_kv_idx", "hsv_select_workspace_bytes", "hsv_tree_position_ids",
                  "hsv_accept_path"):
         getattr(lib, name).restype = ctypes.c_int

@@ -28,6 +28,10 @@
 // blocks ahead, so no load the compiler tracks ever sits between the DMA
 // waits.  Indices outside [0, c) are masked (a per-block 32-bit validity
 // word taken by ballot when the block's rows are read).
+//
+// Sparse sets over a paged cache: the sequence's block table is copied into
+// LDS once, and every gathered row (index or draft row) goes through it to a
+// 64-bit pool address per lane, so the pool may be of any size.
 #include "common.hpp"
 #include "launch.h"
 
@@ -43,6 +47,7 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 constexpr int kWaves = 4;                     // waves per workgroup, each on its own blocks
 constexpr int kNT = kWaves * 64;
@@ -63,6 +68,10 @@ constexpr int kIdxSlot = 64 * 4;               // one block's row indices (64 la
 constexpr int kIdxBytes = kWaves * 2 * kIdxSlot;
 constexpr int kSmemBytes =
     (kStreamBytes > kEpiBytes ? kStreamBytes : kEpiBytes) + kIdxBytes;
+// sparse over a paged cache: the sequence's block table, after the rest
+constexpr int kTabEntries = 6144;
+constexpr int kTabBytes = kTabEntries * 4;
+static_assert(kSmemBytes + kTabBytes <= 160 * 1024, "LDS of one workgroup");
 
 constexpr float kSumLimit = 65536.f;  // as in attn_dma.hip
 
@@ -76,6 +85,17 @@ __device__ __forceinline__ void dma16(const char *sbase, uint32_t voff, uint32_t
       "global_load_lds_dwordx4 %0, %1"
       :
       : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory", "m0");
+}
+
+// The same with a 64-bit address per lane (gathers from a paged pool).
+__device__ __forceinline__ void dma16p(const char *addr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(addr), "s"(lds_base)
       : "memory", "m0");
 }
 
@@ -103,9 +123,10 @@ __device__ __forceinline__ void wait_vm(int n) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool SPAGED>
 __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  static_assert(SPARSE || !SPAGED, "paged gathers are sparse");
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes + (SPAGED ? kTabBytes : 0)];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -158,7 +179,7 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   const int my_n = wave < n_blocks ? (n_blocks - wave + kWaves - 1) / kWaves : 0;
 
   const bool paged = !SPARSE && P.block_table != nullptr;
-  const int64_t kv_row0 = paged ? 0 : static_cast<int64_t>(bg) * P.cap;
+  const int64_t kv_row0 = (paged || SPAGED) ? 0 : static_cast<int64_t>(bg) * P.cap;
   const char *kbytes = static_cast<const char *>(P.k) + kv_row0 * kRowBytes;
   const char *vbytes = static_cast<const char *>(P.v) + kv_row0 * kRowBytes;
   // Paged cache (dense only): lane l holds the pool block of logical block
@@ -183,6 +204,18 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     return ((static_cast<int64_t>(phys) * P.Hkv + g) * (int64_t{1} << P.block_shift) + in_blk) *
            kRowBytes;
   };
+  // Sparse over a paged cache: pool block of each logical block the rows
+  // [0, c + N) fall in (c + N <= cap, and the plan admits at most
+  // kTabEntries columns), clamped into the pool.
+  const lds_i32 *tab = nullptr;
+  if constexpr (SPAGED) {
+    lds_i32 *t = (lds_i32 *)(smem + kSmemBytes);
+    const int nb = (c + P.N + (1 << P.block_shift) - 1) >> P.block_shift;
+    const int32_t *src = P.block_table + static_cast<int64_t>(b) * P.max_blocks;
+    for (int j = tid; j < nb; j += kNT) t[j] = min(max(src[j], 0), P.n_pool_blocks - 1);
+    __syncthreads();
+    tab = t;
+  }
   lds_char *const lds = (lds_char *)(smem);
   const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave * kWaveLds;
 
@@ -240,6 +273,22 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
       const int rk0 = row_of(lane & 15), rk1 = row_of(16 + (lane & 15));
       const int rv0 = row_of(lane >> 2), rv1 = row_of(16 + (lane >> 2));
       const uint32_t st = ring0 + (k & 1) * kBlockBytes;
+      if constexpr (SPAGED) {
+        // cache row -> byte offset of its pool row (block, KV head g, row)
+        const int sh = P.block_shift;
+        auto pool_off = [&](const int row) -> int64_t {
+          const int64_t blk = static_cast<int64_t>(tab[row >> sh]) * P.Hkv + g;
+          return ((blk << sh) + (row & ((1 << sh) - 1))) * kRowBytes;
+        };
+        const char *kp0 = kbytes + pool_off(rk0), *kp1 = kbytes + pool_off(rk1);
+        const char *vp0 = vbytes + pool_off(rv0), *vp1 = vbytes + pool_off(rv1);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          dma16p((x < 4 ? kp0 : kp1) + k_chunk(x), st + x * 1024);
+          dma16p((x < 4 ? vp0 : vp1) + v_chunk(x), st + kHalfBytes + x * 1024);
+        }
+        return;
+      }
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         dma16(kbytes, static_cast<uint32_t>(x < 4 ? rk0 : rk1) * kRowBytes + k_chunk(x),
@@ -553,13 +602,18 @@ bool dma_small_supports(const Plan &p) {
 
 int dma_small_tile_keys() { return kWaves * kBK; }
 
+int dma_small_table_entries() { return kTabEntries; }
+
 hipError_t launch_attn_partials_dma_small(const Plan &p, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(p.n_slots) * p.B * p.Hkv;
-  if (p.n_sel > 0)
-    hipLaunchKernelGGL(attn_partial_dma_small<true>, dim3(static_cast<unsigned>(blocks)),
+  if (p.n_sel > 0 && p.block_table)
+    hipLaunchKernelGGL((attn_partial_dma_small<true, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kNT), 0, s, p);
+  else if (p.n_sel > 0)
+    hipLaunchKernelGGL((attn_partial_dma_small<true, false>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kNT), 0, s, p);
   else
-    hipLaunchKernelGGL(attn_partial_dma_small<false>, dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((attn_partial_dma_small<false, false>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kNT), 0, s, p);
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ hsv_status check_desc(const hsv_verify_desc *d, bool sparse) {
   if (d->block_size != 0) {
     const int bs = d->block_size;
     if (bs < 64 || bs > (1 << 20) || (bs & (bs - 1)) || d->kv_capacity % bs) return HSV_ERR_SHAPE;
-    if (sparse || (d->flags & HSV_FLAG_NO_PREFIX)) return HSV_ERR_UNSUPPORTED;
+    if (d->flags & HSV_FLAG_NO_PREFIX) return HSV_ERR_UNSUPPORTED;
   }
   if (d->batch < 1 || d->n_draft < 1 || d->n_draft > kMaxDraft) return HSV_ERR_SHAPE;
   if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads) return HSV_ERR_SHAPE;
@@ -131,6 +131,10 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
   p->unified = p->kernel == kKernDma256 || p->kernel == kKernDmaSmall;
   const bool paged = d->block_size > 0;
   if (paged && !p->unified) return HSV_ERR_UNSUPPORTED;
+  // paged sparse: the small-group kernel, with the block table in LDS
+  if (paged && sparse &&
+      (p->kernel != kKernDmaSmall || d->kv_capacity / d->block_size > dma_small_table_entries()))
+    return HSV_ERR_UNSUPPORTED;
   if (p->unified) {
     // One key range per (b, kv head): prefix (or index set) then draft rows.  One workgroup
     // per CU: as many splits as fit in one round of the CUs (splits of a
@@ -147,10 +151,11 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
       if (p->B > 1)
         while (ceil_div(keys, target * tile) > 64 && target * 2 <= kMaxSplits) target *= 2;
     }
-    // Paged: splits of whole 64-key tiles (a tile then lies in one pool
-    // block) spanning at most 33 pool blocks (one table entry per lane).
+    // Paged dense: splits of whole 64-key tiles (a tile then lies in one
+    // pool block) spanning at most 33 pool blocks (one table entry per
+    // lane).  Paged sparse rows are translated one by one: no constraint.
     int64_t quantum = 32;
-    if (paged) {
+    if (paged && !sparse) {
       quantum = 64;
       target = std::max<int64_t>(target, ceil_div(keys, 32 * static_cast<int64_t>(d->block_size)));
       if (target > kMaxSplits) return HSV_ERR_UNSUPPORTED;
@@ -335,6 +340,20 @@ hsv_status hsv_verify_attn_paged(const hsv_verify_desc *d, const void *q, const 
   if (d->block_size == 0) return HSV_ERR_SHAPE;
   if (!block_table) return HSV_ERR_NULL;
   return run_verify(d, false, q, k_pool, v_pool, ctx_lens, parent, anc_mask, nullptr, o, lse,
+                    workspace, workspace_bytes, stream, block_table, n_pool_blocks);
+}
+
+hsv_status hsv_verify_attn_sparse_paged(const hsv_verify_desc *d, const void *q,
+                                        const void *k_pool, const void *v_pool,
+                                        const int32_t *block_table, int32_t n_pool_blocks,
+                                        const int32_t *ctx_lens, const int32_t *parent,
+                                        const uint64_t *anc_mask, const int32_t *kv_idx, void *o,
+                                        float *lse, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  if (!d) return HSV_ERR_NULL;
+  if (d->block_size == 0) return HSV_ERR_SHAPE;
+  if (!block_table) return HSV_ERR_NULL;
+  return run_verify(d, true, q, k_pool, v_pool, ctx_lens, parent, anc_mask, kv_idx, o, lse,
                     workspace, workspace_bytes, stream, block_table, n_pool_blocks);
 }
 

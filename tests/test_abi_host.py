@@ -168,7 +168,11 @@ def test_product_package_does_not_reach_the_oracle():
 @pytest.mark.parametrize("kw,code", [
     (dict(block_size=64), 0), (dict(block_size=256), 0), (dict(block_size=16), 2),
     (dict(block_size=96), 2), (dict(block_size=128, kv_capacity=32832), 2),
-    (dict(block_size=64, n_sel=100), 3),                         # sparse + paged
+    (dict(block_size=64, n_sel=100), 3),                         # sparse, 256 rows: MFMA
+    (dict(block_size=64, n_sel=100, n_draft=8), 0),              # sparse, 32 rows
+    (dict(block_size=64, n_sel=100, n_draft=8, max_ctx=393208, kv_capacity=393216), 0),
+    (dict(block_size=64, n_sel=100, n_draft=8, max_ctx=393216, kv_capacity=393280), 3),
+    (dict(block_size=64, n_sel=100, n_draft=8, flags=2), 3),     # sparse, no prefix
     (dict(block_size=64, flags=2), 3),                           # no prefix
     (dict(block_size=64, n_draft=16, n_q_heads=32), 3),          # 64 rows: MFMA kernel
     (dict(block_size=64, head_dim=64), 3),                       # D 64
@@ -194,6 +198,20 @@ def test_paged_call_argument_errors(hsv):
 
     assert call(d, table=None) == hsv.HSV_ERR_NULL
     assert call(d, n_pool=0) == hsv.HSV_ERR_SHAPE
+
+    ds = _desc(hsv, block_size=64, n_sel=100, n_draft=8)
+    ns = _ws(hsv, ds)[1]
+
+    def call_sparse(desc, table=FAKE, kv_idx=FAKE, n_pool=10):
+        return hsv.lib.hsv_verify_attn_sparse_paged(
+            ctypes.byref(desc), FAKE, FAKE, FAKE, table, n_pool, FAKE, FAKE, None, kv_idx,
+            FAKE, FAKE, FAKE, ctypes.c_size_t(ns), None)
+
+    assert call_sparse(ds, table=None) == hsv.HSV_ERR_NULL
+    assert call_sparse(ds, kv_idx=None) == hsv.HSV_ERR_NULL
+    assert call_sparse(ds, n_pool=0) == hsv.HSV_ERR_SHAPE
+    assert call_sparse(_desc(hsv, n_sel=100, n_draft=8)) == hsv.HSV_ERR_SHAPE  # no block size
+    assert call_sparse(_desc(hsv, block_size=64, n_draft=8)) == hsv.HSV_ERR_SHAPE  # n_sel 0
     assert call(_desc(hsv)) == hsv.HSV_ERR_SHAPE                 # no block size
     # a contiguous call must not carry a block size
     assert _call_dense(hsv, d, ws_bytes=n) == hsv.HSV_ERR_SHAPE
