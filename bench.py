@@ -204,8 +204,9 @@ def measure_selection(hsv, dev, steps: int, warmup: int):
     n_cand = L - sh["n_sink"] - sh["n_recent"]
     nbytes = B * H * (2 * 4 * n_cand + 4 * sh["n_sel"])
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"kernel": "select_filter (every CU streams the maps) + select_lists (exact radix "
-                      "select per sequence and KV head)",
+    return {"kernel": "select_floor (sample floors per sequence and KV head) + select_filter "
+                      "(every CU streams the maps) + select_lists (exact radix select per "
+                      "sequence and KV head)",
             "workload": f"B{B} Hkv{H} L{L} n_sel {sh['n_sel']} (sinks {sh['n_sink']}, "
                         f"window {sh['n_recent']}, draft top {sh['n_draft_top']})",
             "call_us": round(us, 2), "algorithmic_bytes_per_call": nbytes,
@@ -316,13 +317,17 @@ def settled_timing(call, steps: int, warmup: int, dev, settle_ms: float = SETTLE
         g.replay()
     torch.cuda.synchronize()
     one_ms = (time.perf_counter() - t0) * 1e3
-    # further replays back to back (no host wait between them) up to the
-    # settling time
-    n_settle = 1 + max(0, math.ceil((settle_ms - one_ms) / max(one_ms, 1e-3)))
-    with torch.cuda.stream(side):
-        for _ in range(n_settle - 1):
-            g.replay()
-    torch.cuda.synchronize()
+    # further replays back to back (no host wait inside a batch) until the
+    # settling time has passed
+    n_settle = 1
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        left = settle_ms - (time.perf_counter() - t0) * 1e3
+        n = max(1, math.ceil(left / max(one_ms, 1e-3)))
+        with torch.cuda.stream(side):
+            for _ in range(n):
+                g.replay()
+        torch.cuda.synchronize()
+        n_settle += n
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()

@@ -14,25 +14,34 @@
 // (key, then the position inverted) every candidate has a distinct value and
 // "the k best" is "every value at or above the k-th largest".
 //
-// Two launches:
-//  1. select_filter (one 256-thread workgroup per 8192-position chunk of a
-//     row, so every CU streams): from a fixed sample of the row (32 spread
-//     segments of 64 positions) the workgroup finds a floor key for each map
-//     -- the 22-bit prefix of the sample's r-th largest key, r a few standard
-//     deviations above the rank the k-th best would have in the sample -- and
-//     appends the (key, position) pairs of its chunk at or above the floor to
-//     its own slots in the workspace.  Every chunk of a row derives the same
-//     floors from the same sample.
-//  2. select_lists (one 1024-thread workgroup per row): loads a map's short
-//     list into LDS and runs an exact radix select over (key, position).  The
-//     list answers the question whenever at least k listed candidates remain
-//     (for the target: once the draft's picks are removed): then the k-th
-//     best is at or above the floor, and every candidate at or above the
-//     floor was listed.  Otherwise (or if a list overflowed) that map falls
-//     back to a streaming radix select over the whole row.  Either way the
-//     result is the exact one.
-// Both kernels are short loops: the selection is instruction-fetch bound if
-// its code is unrolled over a row held in registers.
+// Rows of up to 65536 positions take three launches, each a short chain of
+// memory round trips:
+//  1. select_floor (one 1024-thread workgroup per row): from a fixed sample
+//     of the row (32 segments of 64 positions spread over it; those inside
+//     the candidate range count) each map gets a floor key -- the 22-bit
+//     prefix of the sample's r-th largest key, r a few standard deviations
+//     above the rank the k-th best would have in the sample -- in two radix
+//     passes that serve both maps.
+//  2. select_filter (one 256-thread workgroup per 8192-position chunk of a
+//     row, both maps at once, so every CU streams): the floor becomes the
+//     smallest score whose key is at or above it, so the chunk is tested
+//     with one float compare per score; the scores that pass (raw bits and
+//     position) are appended to the chunk's own slots in the workspace.
+//  3. select_lists (one 1024-thread workgroup per row): every list slot of
+//     both maps is loaded at once.  Per map the listed keys (the target's
+//     without the draft's picks) move to an LDS list while the histogram of
+//     their top 11 bits is built; that gives the first digit, the next
+//     passes take key bits 10..20 and 0..9 (skipped when every entry left
+//     shares them), and the few entries left sharing the k-th key are
+//     ranked by position directly.  A list answers the question whenever at
+//     least k listed candidates remain: then the k-th best is at or above
+//     the floor, and every candidate at or above the floor was listed.
+//     Otherwise (or if a list overflowed) that map falls back to a streaming
+//     radix select over the row.  Either way the result is the exact one.
+//     Sinks and window go to their known output slots, the picked candidates
+//     to theirs by a prefix sum of bitmap popcounts.
+// Longer rows take select_stream: the streaming select for both maps.
+// Only positions below c - n_recent are read from the score rows.
 #include "common.hpp"
 #include "launch.h"
 
@@ -42,13 +51,21 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kFiltThreads = 256;
-constexpr int kChunk = 8192;        // positions per filter workgroup
-constexpr int kChunkCap = 1024;     // list slots per (chunk, map)
-constexpr int kListCap = 8192;      // list entries a row's select holds in LDS
-constexpr int kMaxChunks = 64;      // rows of up to 2^19 positions
+constexpr int kChunk = 8192;          // positions per filter workgroup
+constexpr int kQuads = kChunk / (4 * kFiltThreads);  // 16-byte loads per thread and map
+constexpr int kChunkCap = 1024;       // list slots per (chunk, map)
+constexpr int kListChunks = 8;        // rows of up to 8 chunks take the list path
+constexpr int kListCap = kListChunks * kChunkCap;
+constexpr int kListMax = kListChunks * kChunk;  // 65536 positions
+constexpr int kWords = kListMax / 32;
+constexpr int kStageCap = 8192;       // index sets staged in LDS for a coalesced write
+constexpr int kTieCap = 256;          // entries sharing the k-th key ranked directly
 constexpr int kSegs = 32, kSegLen = 64, kSample = kSegs * kSegLen;
-constexpr int kBins = 2048;         // 11-bit digits
-constexpr int kPosBits = 19;        // positions < 2^19
+constexpr int kSmpPer = kSample / kSelThreads;
+constexpr int kBins = 2048;           // 11-bit digits
+constexpr int kCopies = 4;            // interleaved copies of the first-digit histogram
+constexpr int kPosBits = 19;          // positions < 2^19
+constexpr uint32_t kPosMask = (1u << kPosBits) - 1;
 constexpr int kBufferFlags = 0x00020000;  // word 3 of a gfx9 buffer resource: 32-bit data
 
 // Order-preserving key: larger score -> larger key; NaN -> 1 (below every
@@ -93,8 +110,10 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 }
 
 // Exclusive prefix sum of `x` over a workgroup of NT threads, in thread
-// order; `total` receives the sum.  Uses `scratch` (NT / 64 words).
-template <int NT>
+// order; `total` receives the sum.  Uses `scratch` (NT / 64 words).  With
+// TAIL the call ends with a barrier, so it may be called again at once;
+// without, the caller must pass a barrier before `scratch` is reused.
+template <int NT, bool TAIL = true>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *scratch,
                                                          uint32_t *total) {
   constexpr int kW = NT / kWave;
@@ -109,23 +128,30 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *s
     if (w < wave) wave_base += s;
     all += s;
   }
-  __syncthreads();
+  if (TAIL) __syncthreads();
   *total = all;
   return wave_base + incl - x;
 }
 
-// Digit search over a histogram of kBins counts (bin-major, COPIES
-// interleaved copies): the bin holding the need-th largest value.  Thread t
+// Where bin b (copy cp) of a histogram with COPIES interleaved copies lives.
+template <int COPIES = 1>
+__device__ __forceinline__ int hslot(uint32_t b, uint32_t cp = 0) {
+  return static_cast<int>(b * COPIES + cp);
+}
+
+// Digit search over a histogram of kBins counts (COPIES interleaved
+// copies): the bin holding the need-th largest value.  Thread t
 // owns kBins/NT bins from kBins-1-(kBins/NT)*t downwards, so thread order is
 // descending bin order.  The one thread whose bin holds it writes *digit,
-// *need_out (the rank inside the bin) and *in_bin (the bin's count); the
-// caller then meets at a barrier.  The histogram must hold at least `need`.
-// Each thread zeroes the bins it read, so after that barrier the histogram
-// is clear for the next pass.
+// *need_out (the rank inside the bin) and *in_bin (the bin's count); no
+// thread does if the histogram holds fewer than `need`.  Returns the
+// histogram's total to every thread.  Each thread zeroes the bins it read.
+// The caller passes a barrier before reading the outputs and before the
+// next call (the scan scratch is reused).
 template <int NT, int COPIES>
-__device__ __forceinline__ void find_digit(uint32_t *hist, uint32_t need, uint32_t *scan,
-                                           uint32_t *digit, uint32_t *need_out,
-                                           uint32_t *in_bin) {
+__device__ __forceinline__ uint32_t find_digit(uint32_t *hist, uint32_t need, uint32_t *scan,
+                                               uint32_t *digit, uint32_t *need_out,
+                                               uint32_t *in_bin) {
   constexpr int kPer = kBins / NT;
   const int top = kBins - 1 - kPer * static_cast<int>(threadIdx.x);
   uint32_t cnt[kPer];
@@ -135,14 +161,15 @@ __device__ __forceinline__ void find_digit(uint32_t *hist, uint32_t need, uint32
     uint32_t s = 0;
 #pragma unroll
     for (int cp = 0; cp < COPIES; ++cp) {
-      s += hist[(top - i) * COPIES + cp];
-      hist[(top - i) * COPIES + cp] = 0u;
+      const int a = hslot<COPIES>(static_cast<uint32_t>(top - i), static_cast<uint32_t>(cp));
+      s += hist[a];
+      hist[a] = 0u;
     }
     cnt[i] = s;
     mine += s;
   }
   uint32_t total;
-  uint32_t above = block_exclusive_scan<NT>(mine, scan, &total);
+  uint32_t above = block_exclusive_scan<NT, false>(mine, scan, &total);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (above < need && need <= above + cnt[i]) {
@@ -152,6 +179,7 @@ __device__ __forceinline__ void find_digit(uint32_t *hist, uint32_t need, uint32
     }
     above += cnt[i];
   }
+  return total;
 }
 
 // ---------------------------------------------------------------------------
@@ -166,7 +194,7 @@ struct StreamShared {
   uint32_t digit, need;
 };
 
-__device__ void select_best(const float *row, int lo, int hi, uint32_t k, uint32_t *bits,
+__device__ __forceinline__ void select_best(const float *row, int lo, int hi, uint32_t k, uint32_t *bits,
                             StreamShared &sh) {
   if (k == 0) return;
   const int tid = threadIdx.x, wave = tid / kWave;
@@ -225,271 +253,25 @@ __device__ void select_best(const float *row, int lo, int hi, uint32_t k, uint32
 }
 
 // ---------------------------------------------------------------------------
-// Filter: floors from the sample, then the chunk's candidates at or above
-// them appended to the chunk's list slots.
+// The sample: 32 segments of 64 consecutive positions spread evenly over the
+// row (all positions when it has at most kSample); only those inside the
+// candidate range count.
 // ---------------------------------------------------------------------------
-struct FiltShared {
-  uint4 keys4[kChunk / 4];          // the chunk's keys
-  uint32_t hist[kBins];
-  uint32_t scan[kFiltThreads / kWave];
-  uint32_t digit, need, in_bin, n_out;
-};
-
-// i-th sample position of a row whose candidates are [lo, lo + n_cand):
-// all of them when there are at most kSample, else 32 segments of 64
-// consecutive positions spread evenly.
-__device__ __forceinline__ int sample_pos(int i, int lo, int n_cand) {
-  if (n_cand <= kSample) return lo + i;
-  const int s = i / kSegLen;
-  return lo + static_cast<int>(static_cast<int64_t>(n_cand - kSegLen) * s / (kSegs - 1)) +
-         i % kSegLen;
+__device__ __forceinline__ int segment_start(int s, int score_len) {
+  return (score_len - kSegLen) * s / (kSegs - 1);  // < 2^19 * 31: no overflow
 }
-
-// Floor key for "the k best of n_cand candidates": the smallest key sharing
-// its top 22 bits with the r-th largest sample key, or 1 (every candidate)
-// when the sample is too small for r.
-__device__ uint32_t sample_floor(const float *row, int lo, int n_cand, int k, FiltShared &sh) {
-  const int tid = threadIdx.x;
-  const int n_smp = min(n_cand, kSample);
-  const float mean = static_cast<float>(k) * n_smp / n_cand;
-  const uint32_t r = static_cast<uint32_t>(ceilf(mean + 3.f * sqrtf(mean) + 8.f));
-  if (r >= static_cast<uint32_t>(n_smp)) return 1u;
-  constexpr int kPer = kSample / kFiltThreads;
-  float v[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)  // unconditional: all loads in flight together
-    v[u] = row[sample_pos(min(tid + kFiltThreads * u, n_smp - 1), lo, n_cand)];
-  uint32_t key[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) key[u] = tid + kFiltThreads * u < n_smp ? order_key(v[u]) : 0u;
-  uint32_t prefix = 0, pmask = 0, need = r;
-  for (int i = tid; i < kBins; i += kFiltThreads) sh.hist[i] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 21 : 10;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      if (key[u] != 0u && (key[u] & pmask) == prefix)
-        atomicAdd(&sh.hist[(key[u] >> shift) & (kBins - 1)], 1u);
-    __syncthreads();
-    find_digit<kFiltThreads, 1>(sh.hist, need, sh.scan, &sh.digit, &sh.need, &sh.in_bin);
-    __syncthreads();
-    prefix |= sh.digit << shift;
-    pmask |= static_cast<uint32_t>(kBins - 1) << shift;
-    need = sh.need;
-  }
-  __syncthreads();  // sh.digit / sh.need are read before anyone rewrites them
-  return max(prefix, 1u);
+__device__ __forceinline__ int sample_pos(int i, int score_len) {
+  if (score_len <= kSample) return i;
+  return segment_start(i / kSegLen, score_len) + i % kSegLen;
 }
-
-__global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
-    const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
-    int n_sel, int n_sink, int n_recent, int n_draft_top, int nch, uint32_t *counts,
-    uint2 *lists) {
-  __shared__ FiltShared sh;
-  const int tid = threadIdx.x, lane = tid % kWave;
-  const int bg = blockIdx.x / nch, ch = blockIdx.x % nch;
-  const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
-  const int n_cand = bd.hi - bd.lo;
-  const int64_t row0 = static_cast<int64_t>(bg) * score_len;
-  const int p_begin = max(ch * kChunk, bd.lo), p_end = min(ch * kChunk + kChunk, bd.hi);
-#pragma unroll 1
-  for (int map = 0; map < 2; ++map) {
-    const int k = map == 0 ? bd.m : min(bd.rest + bd.m, n_cand);
-    uint32_t *count = counts + (static_cast<int64_t>(bg) * nch + ch) * 2 + map;
-    uint2 *list = lists + ((static_cast<int64_t>(bg) * nch + ch) * 2 + map) * kChunkCap;
-    if (k <= 0 || p_end <= p_begin) {
-      if (tid == 0) *count = 0;
-      continue;
-    }
-    const float *row = (map == 0 ? draft : target) + row0;
-    const uint32_t floor = sample_floor(row, bd.lo, n_cand, k, sh);
-    // Stage the chunk's keys (0 outside [p_begin, p_end)): positions
-    // ch*8192 + 4*(tid + 256 u) + e, each thread's eight 16-byte buffer
-    // loads issued unconditionally (dword alignment suffices; a load that
-    // would pass hi is moved back to end at hi, so nothing at or past hi --
-    // hence c -- is read).  A quad that crosses hi is staged as 0 here; its
-    // at most three candidates are appended after the loop.
-    constexpr int kU = kChunk / (4 * kFiltThreads);
-    if (bd.hi >= 4) {
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float *>(row), 0, bd.hi * 4, kBufferFlags);
-      uint32_t x[kU][4];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int p4 = ch * kChunk + 4 * (tid + kFiltThreads * u);
-        const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, min(p4, bd.hi - 4) * 4, 0, 0);
-        x[u][0] = q[0], x[u][1] = q[1], x[u][2] = q[2], x[u][3] = q[3];
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int p4 = ch * kChunk + 4 * (tid + kFiltThreads * u);
-        const bool whole = p4 + 3 < bd.hi;
-        uint32_t kk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int p = p4 + e;
-          kk[e] = (whole && p >= p_begin && p < p_end) ? order_key(__uint_as_float(x[u][e])) : 0u;
-        }
-        sh.keys4[tid + kFiltThreads * u] = make_uint4(kk[0], kk[1], kk[2], kk[3]);
-      }
-    } else {
-      for (int u = tid; u < kChunk / 4; u += kFiltThreads) sh.keys4[u] = make_uint4(0, 0, 0, 0);
-    }
-    if (tid == 0) sh.n_out = 0;
-    __syncthreads();
-    // append the keys at or above the floor (key 0 never is): each wave
-    // counts its survivors, reserves them with one LDS atomic, then writes
-    // them in (u, e, lane) order
-    uint4 kq[kU];
-    uint32_t n_keep = 0;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      kq[u] = sh.keys4[tid + kFiltThreads * u];
-      n_keep += __popcll(__ballot(kq[u].x >= floor)) + __popcll(__ballot(kq[u].y >= floor)) +
-                __popcll(__ballot(kq[u].z >= floor)) + __popcll(__ballot(kq[u].w >= floor));
-    }
-    uint32_t base = 0;
-    if (lane == 0 && n_keep) base = atomicAdd(&sh.n_out, n_keep);
-    base = __shfl(base, 0, kWave);
-    const uint64_t below = (uint64_t{1} << lane) - 1;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int p4 = ch * kChunk + 4 * (tid + kFiltThreads * u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = e == 0 ? kq[u].x : e == 1 ? kq[u].y : e == 2 ? kq[u].z : kq[u].w;
-        const bool keep = key >= floor;
-        const uint64_t bal = __ballot(keep);
-        if (keep) {
-          const uint32_t slot = base + static_cast<uint32_t>(__popcll(bal & below));
-          if (slot < static_cast<uint32_t>(kChunkCap)) list[slot] = make_uint2(key, p4 + e);
-        }
-        base += static_cast<uint32_t>(__popcll(bal));
-      }
-    }
-    // the quad that crosses hi (or, for hi < 4, the whole range): single loads
-    {
-      const int t0 = bd.hi >= 4 ? (bd.hi & ~3) : 0;
-      const int p = t0 + tid;
-      if (tid < 4 && p < bd.hi && p >= p_begin && p < p_end) {
-        const uint32_t key = order_key(row[p]);
-        if (key >= floor) {
-          const uint32_t slot = atomicAdd(&sh.n_out, 1u);
-          if (slot < static_cast<uint32_t>(kChunkCap)) list[slot] = make_uint2(key, p);
-        }
-      }
-    }
-    __syncthreads();
-    if (tid == 0) *count = sh.n_out;
-    __syncthreads();
+__device__ __forceinline__ int sample_in_range(int lo, int hi, int score_len) {
+  if (score_len <= kSample) return max(hi - lo, 0);
+  int n = 0;
+  for (int s = 0; s < kSegs; ++s) {
+    const int a = segment_start(s, score_len);
+    n += max(0, min(a + kSegLen, hi) - max(a, lo));
   }
-}
-
-// ---------------------------------------------------------------------------
-// Per-row select over the lists, the fallback, and the write-out.
-// ---------------------------------------------------------------------------
-struct ListShared {
-  union {
-    StreamShared stream;            // fallback; its histogram doubles as the list's
-    uint32_t hist2[kBins * 2];      // list histogram, 2 interleaved copies
-  };
-  int32_t out_stage[kListCap];      // the sorted set, written out coalesced
-  uint32_t cnt[kMaxChunks];
-  uint32_t scan[kSelWaves];
-  uint32_t digit, need, in_bin, ok;
-};
-
-// Select the k best (k >= 1) of map `map`'s list into `bits`; false (and
-// nothing marked) if the list cannot answer (see the file comment).  Rows of
-// up to kListCap / kChunkCap chunks only: thread t holds slot t of every
-// chunk's list in registers (slots past a chunk's count hold key 0), all
-// loaded in one batch.
-__device__ bool list_select(const uint32_t *counts, const uint2 *lists, int bg, int nch, int map,
-                            uint32_t k, uint32_t *bits, ListShared &sh) {
-  constexpr int kMaxListChunks = kListCap / kChunkCap;
-  static_assert(kChunkCap == kSelThreads, "one slot per thread and chunk");
-  const int tid = threadIdx.x, lane = tid % kWave;
-  if (nch > kMaxListChunks) return false;
-  if (tid < kWave) {
-    const uint32_t n =
-        lane < nch ? counts[(static_cast<int64_t>(bg) * nch + lane) * 2 + map] : 0u;
-    const bool over = __any(n > static_cast<uint32_t>(kChunkCap));
-    uint32_t sum = n;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-    if (lane < nch) sh.cnt[lane] = n;
-    if (lane == 0) sh.ok = !over && sum >= k;
-  }
-  __syncthreads();
-  if (!sh.ok) return false;
-  // all slots of all chunks, loads in flight together (chunks past nch read
-  // the last chunk's slots and are dropped); each thread keeps slot tid of
-  // every chunk in registers.  Positions already chosen (the draft's picks,
-  // for the target) get key 0.
-  const uint2 *src = lists + (static_cast<int64_t>(bg) * nch * 2 + map) * kChunkCap + tid;
-  uint2 e[kMaxListChunks];
-#pragma unroll
-  for (int u = 0; u < kMaxListChunks; ++u)
-    e[u] = src[static_cast<int64_t>(min(u, nch - 1)) * 2 * kChunkCap];
-  uint32_t valid = 0;
-#pragma unroll
-  for (int u = 0; u < kMaxListChunks; ++u) {
-    if (u >= nch || static_cast<uint32_t>(tid) >= sh.cnt[u] ||
-        ((bits[e[u].y >> 5] >> (e[u].y & 31)) & 1u))
-      e[u].x = 0u;
-    valid += e[u].x != 0u;
-  }
-  uint32_t n_valid;
-  block_exclusive_scan<kSelThreads>(valid, sh.scan, &n_valid);
-  if (n_valid < k) return false;
-
-  // radix select over value = (key << 19) | (2^19 - 1 - position): passes of
-  // 11/11/10 key bits, then 11/8 position bits if the k-th key is shared
-  constexpr uint32_t kPosMask = (1u << kPosBits) - 1;
-  const uint32_t copy = static_cast<uint32_t>(lane) & 1u;
-  uint32_t kpre = 0, kmask = 0, ppre = 0, pmask = 0, need = k, in_bin = 0;
-  for (int i = tid; i < kBins * 2; i += kSelThreads) sh.hist2[i] = 0u;
-  __syncthreads();
-  for (int pass = 0; pass < 5; ++pass) {
-    if (pass == 3 && need == in_bin) break;  // every key equal to the k-th is taken
-    const bool on_pos = pass >= 3;
-    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : pass == 3 ? 8 : 0;
-    const uint32_t dmask = pass == 2 ? 1023u : pass == 4 ? 255u : 2047u;
-#pragma unroll
-    for (int u = 0; u < kMaxListChunks; ++u) {
-      const uint32_t inv = kPosMask - e[u].y;
-      if (e[u].x != 0u && (e[u].x & kmask) == kpre && (inv & pmask) == ppre) {
-        const uint32_t d = ((on_pos ? inv : e[u].x) >> shift) & dmask;
-        atomicAdd(&sh.hist2[d * 2 + copy], 1u);
-      }
-    }
-    __syncthreads();
-    find_digit<kSelThreads, 2>(sh.hist2, need, sh.scan, &sh.digit, &sh.need, &sh.in_bin);
-    __syncthreads();
-    if (on_pos) {
-      ppre |= sh.digit << shift;
-      pmask |= dmask << shift;
-    } else {
-      kpre |= sh.digit << shift;
-      kmask |= dmask << shift;
-    }
-    need = sh.need;
-    in_bin = sh.in_bin;
-  }
-  __syncthreads();  // sh.digit / sh.need are read before anyone rewrites them
-  // mark every value at or above the k-th: key above it, or equal key and
-  // (when positions were resolved) position at or before it
-#pragma unroll
-  for (int u = 0; u < kMaxListChunks; ++u) {
-    const uint32_t inv = kPosMask - e[u].y;
-    const bool take =
-        e[u].x != 0u && (e[u].x > kpre || (e[u].x == kpre && (pmask == 0 || inv >= ppre)));
-    if (take) atomicOr(&bits[e[u].y >> 5], 1u << (e[u].y & 31));
-  }
-  __syncthreads();
-  return true;
+  return n;
 }
 
 // Bits of positions [a, b) that fall in the word of positions [p0, p0 + 32).
@@ -500,83 +282,591 @@ __device__ __forceinline__ uint32_t range_bits(int p0, int a, int b) {
   return upto & ~((1u << lo) - 1u);
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
-    const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
-    int n_sel, int n_sink, int n_recent, int n_draft_top, int nch, const uint32_t *counts,
-    const uint2 *lists, int32_t *kv_idx) {
-  extern __shared__ uint32_t bits[];  // ceil(score_len / 32) words
-  __shared__ ListShared sh;
-  const int tid = threadIdx.x;
-  const int bg = blockIdx.x;
-  const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
+// The select's state: value bits resolved so far (key bits under kmask,
+// inverted-position bits under pmask) and the rank still needed inside the
+// current bin of in_bin entries.
+struct SelState {
+  uint32_t kpre, kmask, ppre, pmask, need, in_bin;
+};
 
-  const int words = (bd.c + 31) / 32;
-  for (int w = tid; w < words; w += kSelThreads) {
-    // protected positions: [0, lo) and [hi, c)
-    bits[w] = range_bits(32 * w, 0, bd.lo) | range_bits(32 * w, bd.hi, bd.c);
+__device__ __forceinline__ bool in_prefix(const uint2 v, const SelState &s) {
+  return (v.x & s.kmask) == s.kpre && ((kPosMask - v.y) & s.pmask) == s.ppre;
+}
+
+// Passes 2..5 of the select (key bits 10..20 and 0..9, then inverted
+// position bits 8..18 and 0..7) over entries[0, n) by the whole workgroup;
+// done as soon as every entry of the current bin is taken.  The low-key-bit
+// pass is skipped when every entry left after pass 2 shares those bits
+// (seen during pass 2).  Once the key is resolved, up to kTieCap entries
+// sharing it are ranked by position directly (the need-th lowest is the
+// cut) instead of by the two position passes.  hist (kBins words) must be
+// clear; it is clear again on return.  sh_word[0] / [1] / [5] must hold
+// 0 / ~0 / 0 (or / and of low key bits, tie count); sh_word[2..4] and [6]
+// carry results between threads; tie holds kTieCap positions.
+__device__ void late_passes(const uint2 *entries, int n, uint32_t *hist, uint32_t *scan,
+                            uint32_t *sh_word, uint32_t *tie, SelState &s) {
+  const int tid = threadIdx.x, lane = tid % kWave;
+  uint32_t lo_or = 0u, lo_and = ~0u;
+#pragma unroll 1
+  for (int pass = 1; pass < 5; ++pass) {
+    if (s.need == s.in_bin) break;
+    const bool on_pos = pass >= 3;
+    const int shift = pass == 1 ? 10 : pass == 3 ? 8 : 0;
+    const uint32_t dmask = pass == 2 ? 1023u : pass == 4 ? 255u : 2047u;
+    if (pass == 3 && s.in_bin <= static_cast<uint32_t>(kTieCap)) {
+      // the entries with the k-th key, by position: gather, rank, cut
+#pragma unroll 1
+      for (int i = tid; i < n; i += kSelThreads) {
+        const uint2 v = entries[i];
+        if (v.x == s.kpre) tie[atomicAdd(&sh_word[5], 1u)] = v.y;
+      }
+      __syncthreads();
+      if (tid < static_cast<int>(s.in_bin)) {
+        const uint32_t mine = tie[tid];
+        uint32_t below = 0;
+#pragma unroll 1
+        for (uint32_t j = 0; j < s.in_bin; ++j) below += tie[j] < mine;
+        if (below + 1 == s.need) sh_word[6] = mine;
+      }
+      __syncthreads();
+      s.ppre = kPosMask - sh_word[6];  // positions at or below the cut
+      s.pmask = kPosMask;
+      s.need = s.in_bin = 1u;
+      break;
+    }
+    if (pass == 2) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        lo_or |= __shfl_xor(lo_or, o, kWave);
+        lo_and &= __shfl_xor(lo_and, o, kWave);
+      }
+      if (lane == 0) {
+        atomicOr(&sh_word[0], lo_or);
+        atomicAnd(&sh_word[1], lo_and);
+      }
+      __syncthreads();
+      if (sh_word[0] == sh_word[1]) {
+        // every entry left shares its low 10 key bits
+        s.kpre |= sh_word[0];
+        s.kmask |= 1023u;
+        continue;
+      }
+    }
+#pragma unroll 1
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint2 v = entries[i];
+      if (in_prefix(v, s)) {
+        const uint32_t inv = kPosMask - v.y;
+        atomicAdd(&hist[((on_pos ? inv : v.x) >> shift) & dmask], 1u);
+        if (pass == 1) {
+          // pooled over the sub-bins: a superset of the entries left
+          lo_or |= v.x & 1023u;
+          lo_and &= v.x & 1023u;
+        }
+      }
+    }
+    __syncthreads();
+    find_digit<kSelThreads, 1>(hist, s.need, scan, &sh_word[2], &sh_word[3], &sh_word[4]);
+    __syncthreads();
+    const uint32_t digit = sh_word[2];
+    if (on_pos) {
+      s.ppre |= digit << shift;
+      s.pmask |= dmask << shift;
+    } else {
+      s.kpre |= digit << shift;
+      s.kmask |= dmask << shift;
+    }
+    s.need = sh_word[3];
+    s.in_bin = sh_word[4];
+    __syncthreads();  // sh_word[2..4] are rewritten by the next pass
   }
-  __syncthreads();
+}
 
-  const int64_t row0 = static_cast<int64_t>(bg) * score_len;
-  if (bd.m > 0 &&
-      !list_select(counts, lists, bg, nch, 0, static_cast<uint32_t>(bd.m), bits, sh))
-    select_best(draft + row0, bd.lo, bd.hi, static_cast<uint32_t>(bd.m), bits, sh.stream);
-  if (bd.rest > 0 &&
-      !list_select(counts, lists, bg, nch, 1, static_cast<uint32_t>(bd.rest), bits, sh))
-    select_best(target + row0, bd.lo, bd.hi, static_cast<uint32_t>(bd.rest), bits, sh.stream);
-
-  // ascending compaction: thread t owns a contiguous run of words; sets that
-  // fit are staged in LDS and written out coalesced, with the -1 tail
+// Ascending write-out of the set marked in bits[0, ceil(c / 32)): sinks
+// [0, lo) first, then the picked candidates, then the window [hi, c); the
+// -1 tail.  Staged in LDS (`stage`) when n_sel fits.
+__device__ void write_set(const uint32_t *bits, const Budget &bd, int n_sel, int32_t *dst,
+                          int32_t *stage, uint32_t *scan) {
+  const int tid = threadIdx.x;
+  const int words = (bd.c + 31) / 32;
   const int per = (words + kSelThreads - 1) / kSelThreads;
   const int w0 = min(tid * per, words), w1 = min(w0 + per, words);
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
-  uint32_t total;
-  uint32_t out = block_exclusive_scan<kSelThreads>(cnt, sh.scan, &total);
-  int32_t *dst = kv_idx + static_cast<int64_t>(bg) * n_sel;
-  const bool staged = n_sel <= kListCap;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w] & range_bits(32 * w, bd.lo, bd.hi));
+  uint32_t n_picked;
+  uint32_t out = bd.lo + block_exclusive_scan<kSelThreads>(cnt, scan, &n_picked);
+  const int total = bd.lo + static_cast<int>(n_picked) + (bd.c - bd.hi);
+  const bool staged = n_sel <= kStageCap;
+  auto put = [&](int at, int pos) {
+    if (staged)
+      stage[at] = pos;
+    else
+      dst[at] = pos;
+  };
+  for (int j = tid; j < bd.lo && j < n_sel; j += kSelThreads) put(j, j);
+  for (int j = tid; j < bd.c - bd.hi; j += kSelThreads) {
+    const int at = bd.lo + static_cast<int>(n_picked) + j;
+    if (at < n_sel) put(at, bd.hi + j);
+  }
   for (int w = w0; w < w1; ++w) {
-    const uint32_t v = bits[w];
-    if (staged) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const uint32_t at = out + static_cast<uint32_t>(__popc(v & ((1u << j) - 1u)));
-        if (((v >> j) & 1u) && at < static_cast<uint32_t>(n_sel)) sh.out_stage[at] = 32 * w + j;
-      }
-      out += static_cast<uint32_t>(__popc(v));
-    } else {
-      uint32_t r = v;
-      while (r) {
-        const int j = __ffs(r) - 1;
-        r &= r - 1;
-        if (out < static_cast<uint32_t>(n_sel)) dst[out] = 32 * w + j;
-        ++out;
-      }
+    uint32_t v = bits[w] & range_bits(32 * w, bd.lo, bd.hi);
+    while (v) {
+      const int j = __ffs(v) - 1;
+      v &= v - 1;
+      if (out < static_cast<uint32_t>(n_sel)) put(static_cast<int>(out), 32 * w + j);
+      ++out;
     }
   }
   if (staged) {
     __syncthreads();
-    for (int s = tid; s < n_sel; s += kSelThreads)
-      dst[s] = s < static_cast<int>(total) ? sh.out_stage[s] : -1;
+    for (int s = tid; s < n_sel; s += kSelThreads) dst[s] = s < total ? stage[s] : -1;
   } else {
-    for (int s = static_cast<int>(total) + tid; s < n_sel; s += kSelThreads) dst[s] = -1;
+    for (int s = total + tid; s < n_sel; s += kSelThreads) dst[s] = -1;
   }
 }
 
-int select_chunks(int score_len) { return (score_len + kChunk - 1) / kChunk; }
+// ---------------------------------------------------------------------------
+// Floors (one 1024-thread workgroup per row)
+// ---------------------------------------------------------------------------
+// The smallest score whose key is at or above `floor` (a key >= 2): a score
+// f (not NaN) has key(f) >= floor exactly when f >= that score, and NaN
+// (key 1) compares false.  Above every number's key: NaN (nothing passes).
+__device__ __forceinline__ float floor_score(uint32_t floor) {
+  if (floor >= 0x80000000u) return __uint_as_float(floor & 0x7fffffffu);  // +0 .. +inf, or NaN
+  if (floor <= 0x007fffffu) return -__builtin_huge_valf();                // every number
+  return __uint_as_float(~floor);                                         // -0 .. -max
+}
 
-size_t select_count_bytes(size_t rows, int nch) {
-  return (rows * static_cast<size_t>(nch) * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+// The two maps' shares of the budget, for the floors: the draft's m best,
+// and the target's rest + m best (the draft's picks remove at most m).
+__device__ __forceinline__ void floor_ranks(const Budget &bd, int kk[2]) {
+  kk[0] = bd.m;
+  kk[1] = min(bd.rest + bd.m, bd.hi - bd.lo);
+}
+
+struct FloorShared {
+  uint32_t hist[2][kBins];          // sample histograms of the two maps
+  uint32_t scan[kSelWaves];
+  uint32_t digit[2], need[2];
+};
+
+// Per row and map, the floor key: the 22-bit prefix of the r-th largest
+// in-range sample key (r a few standard deviations above the rank the k-th
+// best candidate would have in the sample), or 1 (every candidate) when the
+// sample is too small for r or the map has no share.  floors[row][map].
+__global__ __launch_bounds__(kSelThreads) void select_floor_kernel(
+    const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
+    int n_sel, int n_sink, int n_recent, int n_draft_top, uint32_t *floors) {
+  __shared__ FloorShared sh;
+  const int tid = threadIdx.x;
+  const int bg = blockIdx.x;
+  const int64_t row0 = static_cast<int64_t>(bg) * score_len;
+  const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
+  const int n_cand = bd.hi - bd.lo;
+  int kk[2];
+  floor_ranks(bd, kk);
+  // the sample, entry tid + 1024 u, through buffer resources that end at hi
+  const __amdgpu_buffer_rsrc_t rs[2] = {
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(draft + row0), 0, bd.hi * 4,
+                                        kBufferFlags),
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(target + row0), 0, bd.hi * 4,
+                                        kBufferFlags)};
+  const int n_smp = min(score_len, kSample);
+  uint32_t key[2][kSmpPer];
+#pragma unroll
+  for (int u = 0; u < kSmpPer; ++u) {
+    const int i = tid + kSelThreads * u;
+    const int p = sample_pos(min(i, n_smp - 1), score_len);
+    const bool in = i < n_smp && p >= bd.lo && p < bd.hi;
+#pragma unroll
+    for (int map = 0; map < 2; ++map) {
+      const uint32_t raw = __builtin_amdgcn_raw_buffer_load_b32(rs[map], p * 4, 0, 0);
+      key[map][u] = in ? order_key(__uint_as_float(raw)) : 0u;
+    }
+  }
+  const int n_in = sample_in_range(bd.lo, bd.hi, score_len);
+  bool use[2];
+  uint32_t need[2];
+#pragma unroll
+  for (int map = 0; map < 2; ++map) {
+    const float mean = kk[map] > 0 ? static_cast<float>(kk[map]) * n_in / n_cand : 0.f;
+    need[map] = static_cast<uint32_t>(ceilf(mean + 3.f * sqrtf(mean) + 8.f));
+    use[map] = kk[map] > 0 && need[map] < static_cast<uint32_t>(n_in);
+  }
+  for (int i = tid; i < 2 * kBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
+  __syncthreads();
+  uint32_t prefix[2] = {0u, 0u}, pmask = 0u;
+  if (use[0] || use[1]) {
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 21 : 10;
+#pragma unroll
+      for (int u = 0; u < kSmpPer; ++u)
+#pragma unroll
+        for (int map = 0; map < 2; ++map)
+          if (use[map] && key[map][u] != 0u && (key[map][u] & pmask) == prefix[map])
+            atomicAdd(&sh.hist[map][(key[map][u] >> shift) & (kBins - 1)], 1u);
+      __syncthreads();
+      // both maps' digit searches share one scan: counts of at most kSample
+      // each, packed in the low and high 16 bits
+      {
+        constexpr int kPer = kBins / kSelThreads;
+        const int top = kBins - 1 - kPer * tid;
+        uint32_t cnt[2][kPer], mine = 0;
+#pragma unroll
+        for (int map = 0; map < 2; ++map)
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) {
+            cnt[map][i] = sh.hist[map][top - i];
+            sh.hist[map][top - i] = 0u;
+            mine += cnt[map][i] << (16 * map);
+          }
+        uint32_t all;
+        const uint32_t above2 = block_exclusive_scan<kSelThreads, false>(mine, sh.scan, &all);
+#pragma unroll
+        for (int map = 0; map < 2; ++map) {
+          uint32_t above = (above2 >> (16 * map)) & 0xffffu;
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) {
+            if (above < need[map] && need[map] <= above + cnt[map][i]) {
+              sh.digit[map] = static_cast<uint32_t>(top - i);
+              sh.need[map] = need[map] - above;
+            }
+            above += cnt[map][i];
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int map = 0; map < 2; ++map) {
+        prefix[map] |= sh.digit[map] << shift;
+        need[map] = sh.need[map];
+      }
+      pmask |= static_cast<uint32_t>(kBins - 1) << shift;
+      __syncthreads();  // sh.digit / sh.need are rewritten by the next pass
+    }
+  }
+  if (tid < 2) floors[2 * bg + tid] = use[tid] ? max(prefix[tid], 1u) : 1u;
+}
+
+// ---------------------------------------------------------------------------
+// Filter (one 256-thread workgroup per 8192-position chunk, both maps)
+// ---------------------------------------------------------------------------
+struct FiltShared {
+  uint4 stage[kChunk / 4];          // one map's chunk scores
+  uint32_t n_out[2];                // list entries of the chunk
+};
+
+__global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
+    const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
+    int n_sel, int n_sink, int n_recent, int n_draft_top, int nch, const uint32_t *floors,
+    uint32_t *counts, uint2 *lists) {
+  __shared__ FiltShared sh;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int bg = blockIdx.x / nch, ch = blockIdx.x % nch;
+  const int64_t row0 = static_cast<int64_t>(bg) * score_len;
+  const float *rows[2] = {draft + row0, target + row0};
+  const int c0 = ch * kChunk;
+  const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
+  const int p_begin = max(c0, bd.lo), p_end = min(c0 + kChunk, bd.hi);
+  int kk[2];
+  floor_ranks(bd, kk);
+  bool want[2];
+#pragma unroll
+  for (int map = 0; map < 2; ++map) want[map] = kk[map] > 0 && p_end > p_begin;
+  uint32_t *count = counts + (static_cast<int64_t>(bg) * nch + ch) * 2;
+  if (!want[0] && !want[1]) {
+    if (tid < 2) count[tid] = 0;
+    return;
+  }
+
+  // The chunk (positions c0 + 4*(tid + 256 u) + e), one 16-byte load per
+  // map and u through buffer resources that end at hi (nothing at or past hi
+  // is read; dword alignment suffices); a load that would pass hi is moved
+  // back to end there and its values are not used, the partial quad at hi is
+  // read with single loads.  Every load is unconditional: the compiler waits
+  // at once for a conditional one.
+  const __amdgpu_buffer_rsrc_t rs[2] = {
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rows[0]), 0, bd.hi * 4, kBufferFlags),
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rows[1]), 0, bd.hi * 4, kBufferFlags)};
+  uint32_t x[2][kQuads][4];
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    const int p4 = c0 + 4 * (tid + kFiltThreads * u);
+    const int off = max(min(p4, bd.hi - 4), 0) * 4;
+#pragma unroll
+    for (int map = 0; map < 2; ++map) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs[map], off, 0, 0);
+      x[map][u][0] = q[0], x[map][u][1] = q[1], x[map][u][2] = q[2], x[map][u][3] = q[3];
+    }
+  }
+  const int ep = (bd.hi & ~3) + tid;  // threads 0..3: the partial quad at hi
+  const bool ev = tid < 4 && ep < bd.hi && ep >= p_begin && ep < p_end;
+  uint32_t ex[2];
+#pragma unroll
+  for (int map = 0; map < 2; ++map)
+    ex[map] = __builtin_amdgcn_raw_buffer_load_b32(rs[map], (ev ? ep : 0) * 4, 0, 0);
+  if (tid < 2) sh.n_out[tid] = 0u;
+
+  // the floors as scores: a score passes when it compares >= fl (all:
+  // floor 1, every candidate, NaN included)
+  float fl[2];
+  bool all[2];
+#pragma unroll
+  for (int map = 0; map < 2; ++map) {
+    const uint32_t floor = floors[2 * bg + map];
+    all[map] = floor <= 1u;
+    fl[map] = floor_score(max(floor, 2u));
+  }
+  // per map, this thread's passing scores as a 32-bit mask (bit 4u + e)
+  const bool inside = c0 >= bd.lo && c0 + kChunk <= bd.hi;  // every quad whole and in range
+  uint32_t mask[2] = {0u, 0u};
+#pragma unroll
+  for (int map = 0; map < 2; ++map) {
+    if (!want[map]) continue;
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      const int p4 = c0 + 4 * (tid + kFiltThreads * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = __uint_as_float(x[map][u][e]);
+        bool pass = all[map] || f >= fl[map];
+        if (!inside) pass = pass && p4 + 3 < bd.hi && p4 + e >= p_begin && p4 + e < p_end;
+        mask[map] |= pass ? 1u << (4 * u + e) : 0u;
+      }
+    }
+  }
+  bool epass[2];
+#pragma unroll
+  for (int map = 0; map < 2; ++map)
+    epass[map] = want[map] && ev && (all[map] || __uint_as_float(ex[map]) >= fl[map]);
+  __syncthreads();  // sh.n_out is clear
+  // this wave's slots, reserved with one LDS atomic per map
+  uint32_t slot[2];
+#pragma unroll
+  for (int map = 0; map < 2; ++map) {
+    const uint32_t n = static_cast<uint32_t>(__popc(mask[map])) + (epass[map] ? 1u : 0u);
+    const uint32_t incl = wave_inclusive_scan(n);
+    uint32_t base = 0;
+    if (lane == kWave - 1 && incl != 0u) base = atomicAdd(&sh.n_out[map], incl);
+    slot[map] = __shfl(base, kWave - 1, kWave) + incl - n;
+  }
+  // per map: its chunk scores into LDS, then each thread appends its
+  // passing ones from there (raw score bits and position)
+#pragma unroll
+  for (int map = 0; map < 2; ++map) {
+    if (!want[map]) continue;
+    __syncthreads();  // the stage is free
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u)
+      sh.stage[tid + kFiltThreads * u] =
+          make_uint4(x[map][u][0], x[map][u][1], x[map][u][2], x[map][u][3]);
+    __syncthreads();
+    uint2 *list = lists + ((static_cast<int64_t>(bg) * nch + ch) * 2 + map) * kChunkCap;
+    const uint32_t *st = reinterpret_cast<const uint32_t *>(&sh.stage[0]);
+    uint32_t m = mask[map], sl = slot[map];
+    while (m) {
+      const int i = __ffs(m) - 1;
+      m &= m - 1;
+      const int q = tid + kFiltThreads * (i >> 2);
+      if (sl < static_cast<uint32_t>(kChunkCap))
+        list[sl] = make_uint2(st[4 * q + (i & 3)], c0 + 4 * q + (i & 3));
+      ++sl;
+    }
+    if (epass[map] && sl < static_cast<uint32_t>(kChunkCap)) list[sl] = make_uint2(ex[map], ep);
+  }
+  __syncthreads();
+  if (tid < 2) count[tid] = want[tid] ? sh.n_out[tid] : 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row select over the lists
+// ---------------------------------------------------------------------------
+struct alignas(16) SelBufs {
+  uint32_t hist4[kBins * kCopies];  // first digit, kCopies interleaved copies
+  uint32_t hist1[kBins];            // later passes
+  uint32_t tie[kTieCap];            // positions of the entries with the k-th key
+};
+struct alignas(16) ListShared {
+  uint32_t bits[kWords];            // chosen positions of the row
+  union {
+    uint2 list[kListCap];           // one map's listed entries (key, position)
+    int32_t out_stage[kStageCap];   // the sorted set, written out coalesced
+  };
+  union {
+    SelBufs s;
+    StreamShared stream;            // the fallback
+  };
+  uint32_t scan[kSelWaves];
+  uint32_t word[8];                 // small results passed between threads
+};
+
+// The exact k best (k >= 1) of list[0, n) into `bits`, with hist4 holding
+// the entries' top-11-key-bit counts (kCopies copies); false (nothing
+// marked) if the list holds fewer than k.  hist4 and hist1 are clear on
+// return.  (A function, not inlined: both maps run the same code.)
+__device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh) {
+  const int tid = threadIdx.x;
+  SelBufs &B = sh.s;
+  const uint2 *list = sh.list;
+  if (tid == 0) {
+    sh.word[0] = 0u;   // or of low key bits
+    sh.word[1] = ~0u;  // and
+    sh.word[5] = 0u;   // tied entries gathered
+  }
+  const uint32_t total =
+      find_digit<kSelThreads, kCopies>(B.hist4, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
+  __syncthreads();
+  if (total < k) return false;
+  SelState s;
+  s.kpre = sh.word[2] << 21;
+  s.kmask = static_cast<uint32_t>(kBins - 1) << 21;
+  s.ppre = s.pmask = 0u;
+  s.need = sh.word[3];
+  s.in_bin = sh.word[4];
+  __syncthreads();  // sh.word[2..4] are rewritten below
+  late_passes(list, n, B.hist1, sh.scan, sh.word, B.tie, s);
+  // every value at or above the k-th: above its bin in the resolved key
+  // bits, or inside it and at or above it in the resolved position bits
+#pragma unroll 1
+  for (int i = tid; i < n; i += kSelThreads) {
+    const uint2 v = list[i];
+    const uint32_t kx = v.x & s.kmask;
+    if (kx > s.kpre || (kx == s.kpre && ((kPosMask - v.y) & s.pmask) >= s.ppre))
+      atomicOr(&sh.bits[v.y >> 5], 1u << (v.y & 31));
+  }
+  __syncthreads();
+  return true;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
+    const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
+    int n_sel, int n_sink, int n_recent, int n_draft_top, int nch, const uint32_t *counts,
+    const uint2 *lists, int32_t *kv_idx) {
+  __shared__ ListShared sh;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int bg = blockIdx.x;
+
+  // Every list slot this thread holds (slot tid of each chunk of both maps:
+  // raw score bits and position) is loaded before anything waits; chunks
+  // past nch repeat the last one and are dropped below.
+  uint2 e[2][kListChunks];
+  {
+    const uint2 *src = lists + static_cast<int64_t>(bg) * nch * 2 * kChunkCap + tid;
+#pragma unroll
+    for (int u = 0; u < kListChunks; ++u)
+#pragma unroll
+      for (int map = 0; map < 2; ++map)
+        e[map][u] = src[(static_cast<int64_t>(min(u, nch - 1)) * 2 + map) * kChunkCap];
+  }
+  const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
+  const int words = (bd.c + 31) / 32;
+  for (int w = tid; w < words; w += kSelThreads)
+    sh.bits[w] = range_bits(32 * w, 0, bd.lo) | range_bits(32 * w, bd.hi, bd.c);
+  // a slot holds an entry below its chunk's count; a count past the slots
+  // means the chunk's list overflowed
+  bool over[2] = {false, false};
+  uint32_t valid[2] = {0u, 0u};
+#pragma unroll
+  for (int u = 0; u < kListChunks; ++u)
+#pragma unroll
+    for (int map = 0; map < 2; ++map) {
+      const uint32_t n = u < nch ? counts[(static_cast<int64_t>(bg) * nch + u) * 2 + map] : 0u;
+      over[map] = over[map] || n > static_cast<uint32_t>(kChunkCap);
+      if (static_cast<uint32_t>(tid) < n) valid[map] |= 1u << u;
+    }
+  __syncthreads();
+
+  // One map's select: its entries (the target's without the draft's picks)
+  // into the LDS list, their top 11 key bits into hist4, then the select,
+  // or the streaming fallback.  Called once per map, so that the draft's
+  // registers are free during the target's.
+  auto run_map = [&](const uint2 (&ev)[kListChunks], uint32_t vmask, bool overflow, int k,
+                     const float *row, bool target_map) {
+    if (k <= 0) return;
+    bool done = false;
+    if (!overflow) {
+      for (int i = tid; i < kBins * (kCopies + 1); i += kSelThreads) sh.s.hist4[i] = 0u;
+      const uint32_t copy = static_cast<uint32_t>(lane) & (kCopies - 1);
+      bool in_u[kListChunks];
+#pragma unroll
+      for (int u = 0; u < kListChunks; ++u) {
+        const bool ok = (vmask >> u) & 1u;
+        const uint32_t py = ok ? ev[u].y : 0u;  // an empty slot's position is not read
+        in_u[u] = ok && !(target_map && ((sh.bits[py >> 5] >> (py & 31)) & 1u));
+      }
+      // each thread's entries go to consecutive list slots (a prefix sum
+      // over the workgroup; the scan's barriers also order the clearing)
+      uint32_t n_mine = 0;
+#pragma unroll
+      for (int u = 0; u < kListChunks; ++u) n_mine += in_u[u] ? 1u : 0u;
+      uint32_t n_list;
+      uint32_t at = block_exclusive_scan<kSelThreads>(n_mine, sh.scan, &n_list);
+#pragma unroll
+      for (int u = 0; u < kListChunks; ++u) {
+        if (!in_u[u]) continue;
+        const uint32_t key = order_key(__uint_as_float(ev[u].x));
+        sh.list[at++] = make_uint2(key, ev[u].y);
+        atomicAdd(&sh.s.hist4[hslot<kCopies>(key >> 21, copy)], 1u);
+      }
+      __syncthreads();
+      done = list_select(static_cast<int>(n_list), static_cast<uint32_t>(k), sh);
+    }
+    if (!done) select_best(row, bd.lo, bd.hi, static_cast<uint32_t>(k), sh.bits, sh.stream);
+  };
+  const int64_t row0 = static_cast<int64_t>(bg) * score_len;
+  run_map(e[0], valid[0], over[0], bd.m, draft + row0, false);
+  run_map(e[1], valid[1], over[1], bd.rest, target + row0, true);
+  write_set(sh.bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.out_stage, sh.scan);
+}
+
+// ---------------------------------------------------------------------------
+// Longer rows: the streaming select for both maps
+// ---------------------------------------------------------------------------
+struct StreamKernelShared {
+  union {
+    StreamShared stream;
+    int32_t out_stage[kStageCap];
+  };
+  uint32_t scan[kSelWaves];
+};
+
+__global__ __launch_bounds__(kSelThreads) void select_stream_kernel(
+    const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
+    int n_sel, int n_sink, int n_recent, int n_draft_top, int32_t *kv_idx) {
+  extern __shared__ uint32_t bits[];  // ceil(score_len / 32) words
+  __shared__ StreamKernelShared sh;
+  const int tid = threadIdx.x;
+  const int bg = blockIdx.x;
+  const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
+  const int words = (bd.c + 31) / 32;
+  for (int w = tid; w < words; w += kSelThreads)
+    bits[w] = range_bits(32 * w, 0, bd.lo) | range_bits(32 * w, bd.hi, bd.c);
+  __syncthreads();
+  const int64_t row0 = static_cast<int64_t>(bg) * score_len;
+  if (bd.m > 0) select_best(draft + row0, bd.lo, bd.hi, static_cast<uint32_t>(bd.m), bits, sh.stream);
+  if (bd.rest > 0)
+    select_best(target + row0, bd.lo, bd.hi, static_cast<uint32_t>(bd.rest), bits, sh.stream);
+  write_set(bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.out_stage, sh.scan);
 }
 
 }  // namespace
 
 int select_max_positions() { return 1 << kPosBits; }
 
+namespace {
+int select_chunks(int score_len) { return (score_len + kChunk - 1) / kChunk; }
+size_t select_count_bytes(size_t rows, int nch) {
+  return (rows * static_cast<size_t>(nch) * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+}
+size_t select_floor_bytes(size_t rows) { return (rows * 2 * sizeof(uint32_t) + 255) / 256 * 256; }
+}  // namespace
+
 size_t select_workspace_bytes(int batch, int hkv, int score_len) {
+  if (score_len > kListMax) return 256;  // the streaming kernel needs none
   const size_t rows = static_cast<size_t>(batch) * hkv;
   const int nch = select_chunks(score_len);
-  return select_count_bytes(rows, nch) +
+  return select_floor_bytes(rows) + select_count_bytes(rows, nch) +
          rows * static_cast<size_t>(nch) * 2 * kChunkCap * sizeof(uint2);
 }
 
@@ -584,20 +874,33 @@ hipError_t launch_select_kv_idx(const float *draft, const float *target, int sco
                                 const int32_t *ctx_lens, int batch, int hkv, int n_sel,
                                 int n_sink, int n_recent, int n_draft_top, int32_t *kv_idx,
                                 void *workspace, hipStream_t s) {
-  const int nch = select_chunks(score_len);
-  if (nch > kMaxChunks) return hipErrorInvalidValue;
+  if (score_len < 1 || score_len > select_max_positions()) return hipErrorInvalidValue;
   const size_t rows = static_cast<size_t>(batch) * hkv;
-  uint32_t *counts = static_cast<uint32_t *>(workspace);
-  uint2 *lists = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) +
+  if (score_len > kListMax) {
+    const size_t lds = static_cast<size_t>((score_len + 31) / 32) * sizeof(uint32_t);
+    hipLaunchKernelGGL(select_stream_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads),
+                       lds, s, draft, target, score_len, ctx_lens, hkv, n_sel, n_sink, n_recent,
+                       n_draft_top, kv_idx);
+    return hipGetLastError();
+  }
+  const int nch = select_chunks(score_len);
+  char *ws = static_cast<char *>(workspace);
+  uint32_t *floors = reinterpret_cast<uint32_t *>(ws);
+  uint32_t *counts = reinterpret_cast<uint32_t *>(ws + select_floor_bytes(rows));
+  uint2 *lists = reinterpret_cast<uint2 *>(ws + select_floor_bytes(rows) +
                                            select_count_bytes(rows, nch));
-  hipLaunchKernelGGL(select_filter_kernel, dim3(static_cast<unsigned>(rows * nch)),
-                     dim3(kFiltThreads), 0, s, draft, target, score_len, ctx_lens, hkv, n_sel,
-                     n_sink, n_recent, n_draft_top, nch, counts, lists);
+  hipLaunchKernelGGL(select_floor_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0,
+                     s, draft, target, score_len, ctx_lens, hkv, n_sel, n_sink, n_recent,
+                     n_draft_top, floors);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = static_cast<size_t>((score_len + 31) / 32) * sizeof(uint32_t);
-  hipLaunchKernelGGL(select_lists_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads),
-                     lds, s, draft, target, score_len, ctx_lens, hkv, n_sel, n_sink, n_recent,
+  hipLaunchKernelGGL(select_filter_kernel, dim3(static_cast<unsigned>(rows * nch)),
+                     dim3(kFiltThreads), 0, s, draft, target, score_len, ctx_lens, hkv, n_sel,
+                     n_sink, n_recent, n_draft_top, nch, floors, counts, lists);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_lists_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0,
+                     s, draft, target, score_len, ctx_lens, hkv, n_sel, n_sink, n_recent,
                      n_draft_top, nch, counts, lists, kv_idx);
   return hipGetLastError();
 }

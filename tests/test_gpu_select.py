@@ -6,7 +6,8 @@ Cases: the 65536-position, 8 x 8 (sequence, KV head) shape of the sparse
 workload with bf16-precision maps (many equal scores); ragged contexts down
 to 0 and below the budget; NaN, +-0 and +-inf scores; a few distinct values
 only; the corner budgets (no draft share, draft share beyond the budget, no
-sinks or window, budget equal to the context); the largest score row.
+sinks or window, budget equal to the context); the largest score row;
+full-precision scores and planted ties at the k-th rank.
 """
 
 import numpy as np
@@ -48,6 +49,27 @@ def test_full_size_importance_maps(hsv, gpu):
     draft, target = synth.importance_maps(rng, ctx, 8, 65536)
     _check(hsv, gpu, draft, target, ctx, "B8 Hkv8 L65536 n_sel 4096",
            n_sel=4096, n_sink=4, n_recent=512, n_draft_top=1790)
+
+
+def test_full_precision_and_planted_ties(hsv, gpu):
+    # fp32 scores using every mantissa bit (the low-key-bit pass runs), and
+    # rows where 150 (ranked directly by position) or 400 (position passes)
+    # candidates share the draft score at the n_draft_top-th rank
+    rng = np.random.Generator(np.random.PCG64(515))
+    B, H, L = 2, 4, 65536
+    n_sink, n_recent, m = 4, 512, 1790
+    draft = rng.random((B, H, L), dtype=np.float32)
+    target = rng.random((B, H, L), dtype=np.float32)
+    cand = np.arange(n_sink, L - n_recent)
+    for g, n_tied in ((0, 150), (1, 400), (2, 40)):
+        row = draft[0, g]
+        v = np.sort(row[cand])[-m]
+        row[rng.choice(cand, n_tied, replace=False)] = v
+        trow = target[1, g]
+        trow[rng.choice(cand, n_tied, replace=False)] = np.sort(trow[cand])[-(4096 - 516 - m)]
+    ctx = np.full(B, L, np.int32)
+    _check(hsv, gpu, draft, target, ctx, "fp32 scores, planted ties", n_sel=4096,
+           n_sink=n_sink, n_recent=n_recent, n_draft_top=m)
 
 
 def test_ragged_contexts(hsv, gpu):
@@ -121,26 +143,28 @@ def test_rejects_bad_arguments(hsv, gpu):
         hsv.hsv_select_kv_idx(big, big, c, n_sel=4, n_sink=0, n_recent=0, n_draft_top=0)
 
 
-def _sample_positions(lo, hi):
-    # the filter's sample of the candidates [lo, hi): all of them up to 2048,
-    # else 32 segments of 64 consecutive positions spread evenly
-    n = hi - lo
-    if n <= 2048:
-        return np.arange(lo, hi)
-    starts = lo + ((n - 64) * np.arange(32)) // 31
-    return (starts[:, None] + np.arange(64)[None]).reshape(-1)
+def _sample_positions(lo, hi, L):
+    # the floors' sample: 32 segments of 64 consecutive positions spread
+    # over the row of L positions (all of them up to 2048), those in [lo, hi)
+    if L <= 2048:
+        pos = np.arange(L)
+    else:
+        starts = ((L - 64) * np.arange(32)) // 31
+        pos = (starts[:, None] + np.arange(64)[None]).reshape(-1)
+    return pos[(pos >= lo) & (pos < hi)]
 
 
 def test_sample_defeating_maps(hsv, gpu):
     # Row 0: the only large scores sit on 500 sampled positions, so the floor
     # leaves fewer than k candidates: both maps must fall back to the
     # streaming select.  Row 1: 3000 large scores off the sample, packed
-    # into one 8192-position chunk: its list overflows, again a fallback.
+    # into one 8192-position chunk: its list (1024 slots) overflows, again a
+    # fallback.
     # Row 2: no planted values (the list path).
     L, n_sink, n_recent = 65536, 4, 512
     rng = np.random.Generator(np.random.PCG64(511))
     lo, hi = n_sink, L - n_recent
-    sampled = _sample_positions(lo, hi)
+    sampled = _sample_positions(lo, hi, L)
     off = np.setdiff1d(np.arange(lo, hi), sampled)
     draft = rng.random((3, 1, L), dtype=np.float32)
     target = rng.random((3, 1, L), dtype=np.float32)
