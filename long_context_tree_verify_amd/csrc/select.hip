@@ -14,8 +14,8 @@
 // (key, then the position inverted) every candidate has a distinct value and
 // "the k best" is "every value at or above the k-th largest".
 //
-// Rows of up to 65536 positions take three launches, each a short chain of
-// memory round trips:
+// Rows of up to 73728 positions (a 64k context and its draft rows) take
+// three launches, each a short chain of memory round trips:
 //  1. select_floor (one 1024-thread workgroup per row): from a fixed sample
 //     of the row (32 segments of 64 positions spread over it; those inside
 //     the candidate range count) each map gets a floor key -- the 22-bit
@@ -36,8 +36,10 @@
 //     ranked by position directly.  A list answers the question whenever at
 //     least k listed candidates remain: then the k-th best is at or above
 //     the floor, and every candidate at or above the floor was listed.
-//     Otherwise (or if a list overflowed) that map falls back to a streaming
-//     radix select over the row.  Either way the result is the exact one.
+//     Otherwise (or if a list overflowed, or candidates lie past the first
+//     65536 positions, which have no list slots) that map falls back to a
+//     streaming radix select over the row.  Either way the result is the
+//     exact one.
 //     Sinks and window go to their known output slots, the picked candidates
 //     to theirs by a prefix sum of bitmap popcounts.
 // Longer rows take select_stream: the streaming select for both maps.
@@ -56,8 +58,11 @@ constexpr int kQuads = kChunk / (4 * kFiltThreads);  // 16-byte loads per thread
 constexpr int kChunkCap = 1024;       // list slots per (chunk, map)
 constexpr int kListChunks = 8;        // rows of up to 8 chunks take the list path
 constexpr int kListCap = kListChunks * kChunkCap;
-constexpr int kListMax = kListChunks * kChunk;  // 65536 positions
-constexpr int kWords = kListMax / 32;
+constexpr int kListMax = kListChunks * kChunk;  // 65536 positions with list slots
+constexpr int kBitsMax = kListMax + kChunk;     // rows the list path takes (a 64k context plus
+                                                // its draft rows); entries past kListMax go to
+                                                // the streaming fallback
+constexpr int kWords = kBitsMax / 32;
 constexpr int kStageCap = 8192;       // index sets staged in LDS for a coalesced write
 constexpr int kTieCap = 256;          // entries sharing the k-th key ranked directly
 constexpr int kSegs = 32, kSegLen = 64, kSample = kSegs * kSegLen;
@@ -764,7 +769,8 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
   for (int w = tid; w < words; w += kSelThreads)
     sh.bits[w] = range_bits(32 * w, 0, bd.lo) | range_bits(32 * w, bd.hi, bd.c);
   // a slot holds an entry below its chunk's count; a count past the slots
-  // means the chunk's list overflowed
+  // means the chunk's list overflowed, and so does any entry in a chunk
+  // past the first kListChunks (no slots here for it)
   bool over[2] = {false, false};
   uint32_t valid[2] = {0u, 0u};
 #pragma unroll
@@ -775,6 +781,10 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
       over[map] = over[map] || n > static_cast<uint32_t>(kChunkCap);
       if (static_cast<uint32_t>(tid) < n) valid[map] |= 1u << u;
     }
+  for (int u = kListChunks; u < nch; ++u)
+#pragma unroll
+    for (int map = 0; map < 2; ++map)
+      over[map] = over[map] || counts[(static_cast<int64_t>(bg) * nch + u) * 2 + map] != 0u;
   __syncthreads();
 
   // One map's select: its entries (the target's without the draft's picks)
@@ -863,7 +873,7 @@ size_t select_floor_bytes(size_t rows) { return (rows * 2 * sizeof(uint32_t) + 2
 }  // namespace
 
 size_t select_workspace_bytes(int batch, int hkv, int score_len) {
-  if (score_len > kListMax) return 256;  // the streaming kernel needs none
+  if (score_len > kBitsMax) return 256;  // the streaming kernel needs none
   const size_t rows = static_cast<size_t>(batch) * hkv;
   const int nch = select_chunks(score_len);
   return select_floor_bytes(rows) + select_count_bytes(rows, nch) +
@@ -876,7 +886,7 @@ hipError_t launch_select_kv_idx(const float *draft, const float *target, int sco
                                 void *workspace, hipStream_t s) {
   if (score_len < 1 || score_len > select_max_positions()) return hipErrorInvalidValue;
   const size_t rows = static_cast<size_t>(batch) * hkv;
-  if (score_len > kListMax) {
+  if (score_len > kBitsMax) {
     const size_t lds = static_cast<size_t>((score_len + 31) / 32) * sizeof(uint32_t);
     hipLaunchKernelGGL(select_stream_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads),
                        lds, s, draft, target, score_len, ctx_lens, hkv, n_sel, n_sink, n_recent,

@@ -132,6 +132,20 @@ def test_largest_row(hsv, gpu):
            n_draft_top=3000)
 
 
+def test_rows_past_64k(hsv, gpu):
+    # score rows of a 64k context plus its 8 draft rows (65544 positions):
+    # with a 512-position window the candidates end before 65536 (the list
+    # path); without one they reach past it (the streaming fallback there)
+    rng = np.random.Generator(np.random.PCG64(516))
+    L = 65544
+    ctx = np.array([65536, 65544, 65540, 60000], np.int32)
+    draft, target = synth.importance_maps(rng, ctx, 2, L)
+    _check(hsv, gpu, draft, target, ctx, "L 65544", n_sel=4096, n_sink=4, n_recent=512,
+           n_draft_top=1790)
+    _check(hsv, gpu, draft, target, ctx, "L 65544, no window", n_sel=4096, n_sink=4,
+           n_recent=0, n_draft_top=1790)
+
+
 def test_rejects_bad_arguments(hsv, gpu):
     import torch
     d = torch.zeros((1, 1, 16), dtype=torch.float32, device=gpu)

@@ -152,7 +152,7 @@ def test_wide_tree_other_kernels(hsv, gpu, case):
     # block-parallel masks (bits above the row's own index)
     N = inp.wl.n_draft
     blk = np.broadcast_to(synth.block_masks(N, 40), (inp.wl.batch,) + synth.block_masks(N, 40).shape)
-    blk = np.array(blk, copy=True)
+    blk = np.array(blk, order="C", copy=True)  # writable, C-ordered (not the broadcast view)
     o, lse = run_hip(hsv, inp, dev, parent=None,
                      anc=torch.from_numpy(blk.view(np.int64)).to(gpu))
     ob, lb = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, anc_mask=blk, bf16=inp.is_bf16)
