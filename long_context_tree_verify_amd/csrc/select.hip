@@ -269,13 +269,14 @@ __device__ __forceinline__ int sample_pos(int i, int score_len) {
   if (score_len <= kSample) return i;
   return segment_start(i / kSegLen, score_len) + i % kSegLen;
 }
+// (Lane s of every wave takes segment s; a wave sum adds them up.)
 __device__ __forceinline__ int sample_in_range(int lo, int hi, int score_len) {
   if (score_len <= kSample) return max(hi - lo, 0);
-  int n = 0;
-  for (int s = 0; s < kSegs; ++s) {
-    const int a = segment_start(s, score_len);
-    n += max(0, min(a + kSegLen, hi) - max(a, lo));
-  }
+  const int s = static_cast<int>(threadIdx.x % kWave);
+  const int a = segment_start(s, score_len);
+  int n = s < kSegs ? max(0, min(a + kSegLen, hi) - max(a, lo)) : 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o, kWave);
   return n;
 }
 
