@@ -65,6 +65,7 @@ constexpr int kBitsMax = kListMax + kChunk;     // rows the list path takes (a 6
 constexpr int kWords = kBitsMax / 32;
 constexpr int kStageCap = 8192;       // index sets staged in LDS for a coalesced write
 constexpr int kTieCap = 256;          // entries sharing the k-th key ranked directly
+constexpr int kRankCap = 256;         // entries of the k-th value's floor-relative bin ranked directly
 constexpr int kSegs = 32, kSegLen = 64, kSample = kSegs * kSegLen;
 constexpr int kSmpPer = kSample / kSelThreads;
 constexpr int kBins = 2048;           // 11-bit digits
@@ -453,13 +454,17 @@ __device__ __forceinline__ void floor_ranks(const Budget &bd, int kk[2]) {
 struct FloorShared {
   uint32_t hist[2][kBins];          // sample histograms of the two maps
   uint32_t scan[kSelWaves];
-  uint32_t digit[2], need[2];
+  uint32_t digit[2], need[2], digit_hi[2];
 };
 
 // Per row and map, the floor key: the 22-bit prefix of the r-th largest
 // in-range sample key (r a few standard deviations above the rank the k-th
 // best candidate would have in the sample), or 1 (every candidate) when the
-// sample is too small for r or the map has no share.  floors[row][map].
+// sample is too small for r or the map has no share.  With it a shift s:
+// the top of the 11-bit bin of the r'-th largest sample key (r' as many
+// deviations below that rank) is an upper estimate U of the k-th best, and
+// (U - floor) >> s < 1024, so floor-relative bins (key - floor) >> s split
+// [floor, U] into at most 1024 bins.  floors[row][map] = {floor, s}.
 __global__ __launch_bounds__(kSelThreads) void select_floor_kernel(
     const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
     int n_sel, int n_sink, int n_recent, int n_draft_top, uint32_t *floors) {
@@ -492,11 +497,12 @@ __global__ __launch_bounds__(kSelThreads) void select_floor_kernel(
   }
   const int n_in = sample_in_range(bd.lo, bd.hi, score_len);
   bool use[2];
-  uint32_t need[2];
+  uint32_t need[2], need_hi[2];
 #pragma unroll
   for (int map = 0; map < 2; ++map) {
     const float mean = kk[map] > 0 ? static_cast<float>(kk[map]) * n_in / n_cand : 0.f;
     need[map] = static_cast<uint32_t>(ceilf(mean + 3.f * sqrtf(mean) + 8.f));
+    need_hi[map] = static_cast<uint32_t>(fmaxf(1.f, floorf(mean - 3.f * sqrtf(mean) - 8.f)));
     use[map] = kk[map] > 0 && need[map] < static_cast<uint32_t>(n_in);
   }
   for (int i = tid; i < 2 * kBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
@@ -538,6 +544,8 @@ __global__ __launch_bounds__(kSelThreads) void select_floor_kernel(
               sh.digit[map] = static_cast<uint32_t>(top - i);
               sh.need[map] = need[map] - above;
             }
+            if (pass == 0 && above < need_hi[map] && need_hi[map] <= above + cnt[map][i])
+              sh.digit_hi[map] = static_cast<uint32_t>(top - i);
             above += cnt[map][i];
           }
         }
@@ -552,7 +560,19 @@ __global__ __launch_bounds__(kSelThreads) void select_floor_kernel(
       __syncthreads();  // sh.digit / sh.need are rewritten by the next pass
     }
   }
-  if (tid < 2) floors[2 * bg + tid] = use[tid] ? max(prefix[tid], 1u) : 1u;
+  if (tid < 2) {
+    const int map = tid;
+    uint32_t floor = 1u, sft = 21u;  // no floor: bins of the top 11 key bits
+    if (use[map]) {
+      floor = max(prefix[map], 1u);
+      const uint32_t dh = sh.digit_hi[map];
+      const uint32_t upper = dh >= kBins - 1 ? ~0u : ((dh + 1u) << 21) - 1u;
+      const uint32_t span = upper - floor;  // the r'-th key is at or above the r-th
+      sft = static_cast<uint32_t>(max(0, (31 - __builtin_clz(span | 1u)) - 9));
+    }
+    floors[4 * bg + 2 * map] = floor;
+    floors[4 * bg + 2 * map + 1] = sft;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -620,7 +640,7 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
   bool all[2];
 #pragma unroll
   for (int map = 0; map < 2; ++map) {
-    const uint32_t floor = floors[2 * bg + map];
+    const uint32_t floor = floors[4 * bg + 2 * map];
     all[map] = floor <= 1u;
     fl[map] = floor_score(max(floor, 2u));
   }
@@ -692,6 +712,7 @@ struct alignas(16) SelBufs {
   uint32_t hist4[kBins * kCopies];  // first digit, kCopies interleaved copies
   uint32_t hist1[kBins];            // later passes
   uint32_t tie[kTieCap];            // positions of the entries with the k-th key
+  uint2 cand[kRankCap];             // entries of the k-th value's floor-relative bin
 };
 struct alignas(16) ListShared {
   uint32_t bits[kWords];            // chosen positions of the row
@@ -707,31 +728,85 @@ struct alignas(16) ListShared {
   uint32_t word[8];                 // small results passed between threads
 };
 
+// Floor-relative bin of a listed key (every listed key is at or above the
+// floor): (key - floor) >> sft, the keys past the upper estimate in the last
+// bin.
+__device__ __forceinline__ uint32_t rel_bin(uint32_t key, uint32_t floor, uint32_t sft) {
+  return min((key - floor) >> sft, static_cast<uint32_t>(kBins - 1));
+}
+
+// Value order of two listed entries: key, then the lower position.
+__device__ __forceinline__ bool value_above(const uint2 a, const uint2 b) {
+  return a.x > b.x || (a.x == b.x && a.y < b.y);
+}
+
 // The exact k best (k >= 1) of list[0, n) into `bits`, with hist4 holding
-// the entries' top-11-key-bit counts (kCopies copies); false (nothing
-// marked) if the list holds fewer than k.  hist4 and hist1 are clear on
-// return.  (A function, not inlined: both maps run the same code.)
-__device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh) {
-  const int tid = threadIdx.x;
+// the entries' floor-relative bin counts (kCopies copies); false (nothing
+// marked) if the list holds fewer than k.  When the k-th value's bin holds
+// at most kRankCap entries, those are ranked directly; otherwise the bins
+// are rebuilt from the top 11 key bits and the radix passes resolve the
+// rest.  hist4 and hist1 are clear on return.  (A
+// function, not inlined: both maps run the same code.)
+__device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint32_t floor,
+                                         uint32_t sft) {
+  const int tid = threadIdx.x, lane = tid % kWave;
   SelBufs &B = sh.s;
   const uint2 *list = sh.list;
   if (tid == 0) {
     sh.word[0] = 0u;   // or of low key bits
     sh.word[1] = ~0u;  // and
-    sh.word[5] = 0u;   // tied entries gathered
+    sh.word[5] = 0u;   // entries gathered (bin, then ties)
   }
   const uint32_t total =
       find_digit<kSelThreads, kCopies>(B.hist4, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
   __syncthreads();
   if (total < k) return false;
   SelState s;
-  s.kpre = sh.word[2] << 21;
-  s.kmask = static_cast<uint32_t>(kBins - 1) << 21;
-  s.ppre = s.pmask = 0u;
   s.need = sh.word[3];
   s.in_bin = sh.word[4];
+  const uint32_t d1 = sh.word[2];
   __syncthreads();  // sh.word[2..4] are rewritten below
-  late_passes(list, n, B.hist1, sh.scan, sh.word, B.tie, s);
+  if (s.in_bin <= static_cast<uint32_t>(kRankCap)) {
+    // the bin's entries, ranked by value: the need-th is the k-th overall
+#pragma unroll 1
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint2 v = list[i];
+      if (rel_bin(v.x, floor, sft) == d1) B.cand[atomicAdd(&sh.word[5], 1u)] = v;
+    }
+    __syncthreads();
+    if (tid < static_cast<int>(s.in_bin)) {
+      const uint2 mine = B.cand[tid];
+      uint32_t above = 0;
+#pragma unroll 1
+      for (uint32_t j = 0; j < s.in_bin; ++j) above += value_above(B.cand[j], mine);
+      if (above + 1 == s.need) {
+        sh.word[2] = mine.x;
+        sh.word[3] = mine.y;
+      }
+    }
+    __syncthreads();
+    s.kpre = sh.word[2];
+    s.kmask = ~0u;
+    s.ppre = kPosMask - sh.word[3];  // positions at or below the k-th's
+    s.pmask = kPosMask;
+  } else {
+    // bins of the top 11 key bits (hist4 is clear: the search read it all)
+    const uint32_t copy = static_cast<uint32_t>(lane) & (kCopies - 1);
+#pragma unroll 1
+    for (int i = tid; i < n; i += kSelThreads)
+      atomicAdd(&B.hist4[hslot<kCopies>(list[i].x >> 21, copy)], 1u);
+    if (tid == 0) sh.word[5] = 0u;
+    __syncthreads();
+    find_digit<kSelThreads, kCopies>(B.hist4, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
+    __syncthreads();
+    s.kpre = sh.word[2] << 21;
+    s.kmask = static_cast<uint32_t>(kBins - 1) << 21;
+    s.ppre = s.pmask = 0u;
+    s.need = sh.word[3];
+    s.in_bin = sh.word[4];
+    __syncthreads();  // sh.word[2..4] are rewritten below
+    late_passes(list, n, B.hist1, sh.scan, sh.word, B.tie, s);
+  }
   // every value at or above the k-th: above its bin in the resolved key
   // bits, or inside it and at or above it in the resolved position bits
 #pragma unroll 1
@@ -747,8 +822,8 @@ __device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh) {
 
 __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
     const float *draft, const float *target, int score_len, const int32_t *ctx_lens, int hkv,
-    int n_sel, int n_sink, int n_recent, int n_draft_top, int nch, const uint32_t *counts,
-    const uint2 *lists, int32_t *kv_idx) {
+    int n_sel, int n_sink, int n_recent, int n_draft_top, int nch, const uint32_t *floors,
+    const uint32_t *counts, const uint2 *lists, int32_t *kv_idx) {
   __shared__ ListShared sh;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int bg = blockIdx.x;
@@ -793,7 +868,7 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
   // or the streaming fallback.  Called once per map, so that the draft's
   // registers are free during the target's.
   auto run_map = [&](const uint2 (&ev)[kListChunks], uint32_t vmask, bool overflow, int k,
-                     const float *row, bool target_map) {
+                     const float *row, bool target_map, uint32_t floor, uint32_t sft) {
     if (k <= 0) return;
     bool done = false;
     if (!overflow) {
@@ -818,16 +893,17 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
         if (!in_u[u]) continue;
         const uint32_t key = order_key(__uint_as_float(ev[u].x));
         sh.list[at++] = make_uint2(key, ev[u].y);
-        atomicAdd(&sh.s.hist4[hslot<kCopies>(key >> 21, copy)], 1u);
+        atomicAdd(&sh.s.hist4[hslot<kCopies>(rel_bin(key, floor, sft), copy)], 1u);
       }
       __syncthreads();
-      done = list_select(static_cast<int>(n_list), static_cast<uint32_t>(k), sh);
+      done = list_select(static_cast<int>(n_list), static_cast<uint32_t>(k), sh, floor, sft);
     }
     if (!done) select_best(row, bd.lo, bd.hi, static_cast<uint32_t>(k), sh.bits, sh.stream);
   };
   const int64_t row0 = static_cast<int64_t>(bg) * score_len;
-  run_map(e[0], valid[0], over[0], bd.m, draft + row0, false);
-  run_map(e[1], valid[1], over[1], bd.rest, target + row0, true);
+  run_map(e[0], valid[0], over[0], bd.m, draft + row0, false, floors[4 * bg], floors[4 * bg + 1]);
+  run_map(e[1], valid[1], over[1], bd.rest, target + row0, true, floors[4 * bg + 2],
+          floors[4 * bg + 3]);
   write_set(sh.bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.out_stage, sh.scan);
 }
 
@@ -870,7 +946,7 @@ int select_chunks(int score_len) { return (score_len + kChunk - 1) / kChunk; }
 size_t select_count_bytes(size_t rows, int nch) {
   return (rows * static_cast<size_t>(nch) * 2 * sizeof(uint32_t) + 255) / 256 * 256;
 }
-size_t select_floor_bytes(size_t rows) { return (rows * 2 * sizeof(uint32_t) + 255) / 256 * 256; }
+size_t select_floor_bytes(size_t rows) { return (rows * 4 * sizeof(uint32_t) + 255) / 256 * 256; }
 }  // namespace
 
 size_t select_workspace_bytes(int batch, int hkv, int score_len) {
@@ -912,7 +988,7 @@ hipError_t launch_select_kv_idx(const float *draft, const float *target, int sco
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_lists_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0,
                      s, draft, target, score_len, ctx_lens, hkv, n_sel, n_sink, n_recent,
-                     n_draft_top, nch, counts, lists, kv_idx);
+                     n_draft_top, nch, floors, counts, lists, kv_idx);
   return hipGetLastError();
 }
 
