@@ -278,7 +278,8 @@ hsv_status hsv_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens,
  * positions are chosen.  Best = higher score; NaN ranks below every number;
  * -0 equals +0; ties go to the lower position.
  * draft_score, target_score [B, Hkv, score_len] float (entries at or past
- * c_b are not read); ctx_lens [B] int32 (device); kv_idx [B, Hkv, n_sel]
+ * c_b do not affect the result; the whole rows may be read);
+ * ctx_lens [B] int32 (device); kv_idx [B, Hkv, n_sel]
  * int32 out, strictly increasing -- if c_b < n_sel the tail is -1.
  * Requires n_sink + n_recent <= n_sel, n_draft_top >= 0 and
  * score_len <= 524288; the chosen set is unique (no randomness).

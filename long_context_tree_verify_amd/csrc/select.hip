@@ -43,7 +43,8 @@
 //     Sinks and window go to their known output slots, the picked candidates
 //     to theirs by a prefix sum of bitmap popcounts.
 // Longer rows take select_stream: the streaming select for both maps.
-// Only positions below c - n_recent are read from the score rows.
+// Scores at or past c do not affect the result (the kernels read the rows
+// without waiting for the context lengths, and drop those positions).
 #include "common.hpp"
 #include "launch.h"
 
@@ -472,17 +473,20 @@ __global__ __launch_bounds__(kSelThreads) void select_floor_kernel(
   const int tid = threadIdx.x;
   const int bg = blockIdx.x;
   const int64_t row0 = static_cast<int64_t>(bg) * score_len;
+  // the sample, entry tid + 1024 u, loaded before the context length is
+  // known (positions outside the candidates are not used)
+  const int n_smp = min(score_len, kSample);
+  uint32_t raw[2][kSmpPer];
+#pragma unroll
+  for (int u = 0; u < kSmpPer; ++u) {
+    const int p = sample_pos(min(tid + kSelThreads * u, n_smp - 1), score_len);
+    raw[0][u] = __float_as_uint(draft[row0 + p]);
+    raw[1][u] = __float_as_uint(target[row0 + p]);
+  }
   const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
   const int n_cand = bd.hi - bd.lo;
   int kk[2];
   floor_ranks(bd, kk);
-  // the sample, entry tid + 1024 u, through buffer resources that end at hi
-  const __amdgpu_buffer_rsrc_t rs[2] = {
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(draft + row0), 0, bd.hi * 4,
-                                        kBufferFlags),
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(target + row0), 0, bd.hi * 4,
-                                        kBufferFlags)};
-  const int n_smp = min(score_len, kSample);
   uint32_t key[2][kSmpPer];
 #pragma unroll
   for (int u = 0; u < kSmpPer; ++u) {
@@ -490,10 +494,8 @@ __global__ __launch_bounds__(kSelThreads) void select_floor_kernel(
     const int p = sample_pos(min(i, n_smp - 1), score_len);
     const bool in = i < n_smp && p >= bd.lo && p < bd.hi;
 #pragma unroll
-    for (int map = 0; map < 2; ++map) {
-      const uint32_t raw = __builtin_amdgcn_raw_buffer_load_b32(rs[map], p * 4, 0, 0);
-      key[map][u] = in ? order_key(__uint_as_float(raw)) : 0u;
-    }
+    for (int map = 0; map < 2; ++map)
+      key[map][u] = in ? order_key(__uint_as_float(raw[map][u])) : 0u;
   }
   const int n_in = sample_in_range(bd.lo, bd.hi, score_len);
   bool use[2];
@@ -593,6 +595,36 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
   const int64_t row0 = static_cast<int64_t>(bg) * score_len;
   const float *rows[2] = {draft + row0, target + row0};
   const int c0 = ch * kChunk;
+
+  // The chunk (positions c0 + 4*(tid + 256 u) + e), one 16-byte load per
+  // map and u through buffer resources that end at the row's end (dword
+  // alignment suffices), issued before the context length is known;
+  // positions outside the candidates are loaded but not used.  A load that
+  // would pass the row's end is moved back to end there and its values are
+  // not used; the partial quad at the end is read with single loads.  Every
+  // load is unconditional: the compiler waits at once for a conditional one.
+  const __amdgpu_buffer_rsrc_t rs[2] = {
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rows[0]), 0, score_len * 4,
+                                        kBufferFlags),
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rows[1]), 0, score_len * 4,
+                                        kBufferFlags)};
+  uint32_t x[2][kQuads][4];
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    const int p4 = c0 + 4 * (tid + kFiltThreads * u);
+    const int off = max(min(p4, score_len - 4), 0) * 4;
+#pragma unroll
+    for (int map = 0; map < 2; ++map) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs[map], off, 0, 0);
+      x[map][u][0] = q[0], x[map][u][1] = q[1], x[map][u][2] = q[2], x[map][u][3] = q[3];
+    }
+  }
+  const int ep = (score_len & ~3) + tid;  // threads 0..3: the partial quad at the end
+  uint32_t ex[2];
+#pragma unroll
+  for (int map = 0; map < 2; ++map)
+    ex[map] = __builtin_amdgcn_raw_buffer_load_b32(rs[map], (tid < 4 ? ep : 0) * 4, 0, 0);
+
   const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
   const int p_begin = max(c0, bd.lo), p_end = min(c0 + kChunk, bd.hi);
   int kk[2];
@@ -605,33 +637,7 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
     if (tid < 2) count[tid] = 0;
     return;
   }
-
-  // The chunk (positions c0 + 4*(tid + 256 u) + e), one 16-byte load per
-  // map and u through buffer resources that end at hi (nothing at or past hi
-  // is read; dword alignment suffices); a load that would pass hi is moved
-  // back to end there and its values are not used, the partial quad at hi is
-  // read with single loads.  Every load is unconditional: the compiler waits
-  // at once for a conditional one.
-  const __amdgpu_buffer_rsrc_t rs[2] = {
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rows[0]), 0, bd.hi * 4, kBufferFlags),
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rows[1]), 0, bd.hi * 4, kBufferFlags)};
-  uint32_t x[2][kQuads][4];
-#pragma unroll
-  for (int u = 0; u < kQuads; ++u) {
-    const int p4 = c0 + 4 * (tid + kFiltThreads * u);
-    const int off = max(min(p4, bd.hi - 4), 0) * 4;
-#pragma unroll
-    for (int map = 0; map < 2; ++map) {
-      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs[map], off, 0, 0);
-      x[map][u][0] = q[0], x[map][u][1] = q[1], x[map][u][2] = q[2], x[map][u][3] = q[3];
-    }
-  }
-  const int ep = (bd.hi & ~3) + tid;  // threads 0..3: the partial quad at hi
-  const bool ev = tid < 4 && ep < bd.hi && ep >= p_begin && ep < p_end;
-  uint32_t ex[2];
-#pragma unroll
-  for (int map = 0; map < 2; ++map)
-    ex[map] = __builtin_amdgcn_raw_buffer_load_b32(rs[map], (ev ? ep : 0) * 4, 0, 0);
+  const bool ev = tid < 4 && ep < score_len && ep >= p_begin && ep < p_end;
   if (tid < 2) sh.n_out[tid] = 0u;
 
   // the floors as scores: a score passes when it compares >= fl (all:
@@ -645,7 +651,7 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
     fl[map] = floor_score(max(floor, 2u));
   }
   // per map, this thread's passing scores as a 32-bit mask (bit 4u + e)
-  const bool inside = c0 >= bd.lo && c0 + kChunk <= bd.hi;  // every quad whole and in range
+  const bool inside = c0 >= bd.lo && c0 + kChunk <= bd.hi;  // every quad whole and a candidate
   uint32_t mask[2] = {0u, 0u};
 #pragma unroll
   for (int map = 0; map < 2; ++map) {
@@ -657,7 +663,7 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
       for (int e = 0; e < 4; ++e) {
         const float f = __uint_as_float(x[map][u][e]);
         bool pass = all[map] || f >= fl[map];
-        if (!inside) pass = pass && p4 + 3 < bd.hi && p4 + e >= p_begin && p4 + e < p_end;
+        if (!inside) pass = pass && p4 + 3 < score_len && p4 + e >= p_begin && p4 + e < p_end;
         mask[map] |= pass ? 1u << (4 * u + e) : 0u;
       }
     }
