@@ -41,7 +41,7 @@
 //     streaming radix select over the row.  Either way the result is the
 //     exact one.
 //     Sinks and window go to their known output slots, the picked candidates
-//     to theirs by a prefix sum of bitmap popcounts.
+//     to theirs by a prefix sum of bitmap popcounts, written straight out.
 // Longer rows take select_stream: the streaming select for both maps.
 // Scores at or past c do not affect the result (the kernels read the rows
 // without waiting for the context lengths, and drop those positions).
@@ -64,7 +64,6 @@ constexpr int kBitsMax = kListMax + kChunk;     // rows the list path takes (a 6
                                                 // its draft rows); entries past kListMax go to
                                                 // the streaming fallback
 constexpr int kWords = kBitsMax / 32;
-constexpr int kStageCap = 8192;       // index sets staged in LDS for a coalesced write
 constexpr int kTieCap = 256;          // entries sharing the k-th key ranked directly
 constexpr int kRankCap = 256;         // entries of the k-th value's floor-relative bin ranked directly
 constexpr int kSegs = 32, kSegLen = 64, kSample = kSegs * kSegLen;
@@ -392,9 +391,10 @@ __device__ void late_passes(const uint2 *entries, int n, uint32_t *hist, uint32_
 
 // Ascending write-out of the set marked in bits[0, ceil(c / 32)): sinks
 // [0, lo) first, then the picked candidates, then the window [hi, c); the
-// -1 tail.  Staged in LDS (`stage`) when n_sel fits.
+// -1 tail.  Each thread writes its run of positions straight to the output
+// (staging the set in LDS for coalesced stores cost a barrier and more).
 __device__ void write_set(const uint32_t *bits, const Budget &bd, int n_sel, int32_t *dst,
-                          int32_t *stage, uint32_t *scan) {
+                          uint32_t *scan) {
   const int tid = threadIdx.x;
   const int words = (bd.c + 31) / 32;
   const int per = (words + kSelThreads - 1) / kSelThreads;
@@ -404,33 +404,21 @@ __device__ void write_set(const uint32_t *bits, const Budget &bd, int n_sel, int
   uint32_t n_picked;
   uint32_t out = bd.lo + block_exclusive_scan<kSelThreads>(cnt, scan, &n_picked);
   const int total = bd.lo + static_cast<int>(n_picked) + (bd.c - bd.hi);
-  const bool staged = n_sel <= kStageCap;
-  auto put = [&](int at, int pos) {
-    if (staged)
-      stage[at] = pos;
-    else
-      dst[at] = pos;
-  };
-  for (int j = tid; j < bd.lo && j < n_sel; j += kSelThreads) put(j, j);
+  for (int j = tid; j < bd.lo && j < n_sel; j += kSelThreads) dst[j] = j;
   for (int j = tid; j < bd.c - bd.hi; j += kSelThreads) {
     const int at = bd.lo + static_cast<int>(n_picked) + j;
-    if (at < n_sel) put(at, bd.hi + j);
+    if (at < n_sel) dst[at] = bd.hi + j;
   }
   for (int w = w0; w < w1; ++w) {
     uint32_t v = bits[w] & range_bits(32 * w, bd.lo, bd.hi);
     while (v) {
       const int j = __ffs(v) - 1;
       v &= v - 1;
-      if (out < static_cast<uint32_t>(n_sel)) put(static_cast<int>(out), 32 * w + j);
+      if (out < static_cast<uint32_t>(n_sel)) dst[out] = 32 * w + j;
       ++out;
     }
   }
-  if (staged) {
-    __syncthreads();
-    for (int s = tid; s < n_sel; s += kSelThreads) dst[s] = s < total ? stage[s] : -1;
-  } else {
-    for (int s = total + tid; s < n_sel; s += kSelThreads) dst[s] = -1;
-  }
+  for (int s = total + tid; s < n_sel; s += kSelThreads) dst[s] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -722,10 +710,7 @@ struct alignas(16) SelBufs {
 };
 struct alignas(16) ListShared {
   uint32_t bits[kWords];            // chosen positions of the row
-  union {
-    uint2 list[kListCap];           // one map's listed entries (key, position)
-    int32_t out_stage[kStageCap];   // the sorted set, written out coalesced
-  };
+  uint2 list[kListCap];             // one map's listed entries (key, position)
   union {
     SelBufs s;
     StreamShared stream;            // the fallback
@@ -910,17 +895,14 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
   run_map(e[0], valid[0], over[0], bd.m, draft + row0, false, floors[4 * bg], floors[4 * bg + 1]);
   run_map(e[1], valid[1], over[1], bd.rest, target + row0, true, floors[4 * bg + 2],
           floors[4 * bg + 3]);
-  write_set(sh.bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.out_stage, sh.scan);
+  write_set(sh.bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.scan);
 }
 
 // ---------------------------------------------------------------------------
 // Longer rows: the streaming select for both maps
 // ---------------------------------------------------------------------------
 struct StreamKernelShared {
-  union {
-    StreamShared stream;
-    int32_t out_stage[kStageCap];
-  };
+  StreamShared stream;
   uint32_t scan[kSelWaves];
 };
 
@@ -940,7 +922,7 @@ __global__ __launch_bounds__(kSelThreads) void select_stream_kernel(
   if (bd.m > 0) select_best(draft + row0, bd.lo, bd.hi, static_cast<uint32_t>(bd.m), bits, sh.stream);
   if (bd.rest > 0)
     select_best(target + row0, bd.lo, bd.hi, static_cast<uint32_t>(bd.rest), bits, sh.stream);
-  write_set(bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.out_stage, sh.scan);
+  write_set(bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.scan);
 }
 
 }  // namespace
