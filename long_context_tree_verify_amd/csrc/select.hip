@@ -69,7 +69,8 @@ constexpr int kRankCap = 256;         // entries of the k-th value's floor-relat
 constexpr int kSegs = 32, kSegLen = 64, kSample = kSegs * kSegLen;
 constexpr int kSmpPer = kSample / kSelThreads;
 constexpr int kBins = 2048;           // 11-bit digits
-constexpr int kCopies = 4;            // interleaved copies of the first-digit histogram
+constexpr int kCopies = 1;            // copies of the first-digit histogram (the fallback
+                                      // bins could take interleaved ones)
 constexpr int kPosBits = 19;          // positions < 2^19
 constexpr uint32_t kPosMask = (1u << kPosBits) - 1;
 constexpr int kBufferFlags = 0x00020000;  // word 3 of a gfx9 buffer resource: 32-bit data
@@ -703,7 +704,7 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
 // Per-row select over the lists
 // ---------------------------------------------------------------------------
 struct alignas(16) SelBufs {
-  uint32_t hist4[kBins * kCopies];  // first digit, kCopies interleaved copies
+  uint32_t hist_first[kBins * kCopies];  // the first digit
   uint32_t hist1[kBins];            // later passes
   uint32_t tie[kTieCap];            // positions of the entries with the k-th key
   uint2 cand[kRankCap];             // entries of the k-th value's floor-relative bin
@@ -731,12 +732,12 @@ __device__ __forceinline__ bool value_above(const uint2 a, const uint2 b) {
   return a.x > b.x || (a.x == b.x && a.y < b.y);
 }
 
-// The exact k best (k >= 1) of list[0, n) into `bits`, with hist4 holding
+// The exact k best (k >= 1) of list[0, n) into `bits`, with hist_first holding
 // the entries' floor-relative bin counts (kCopies copies); false (nothing
 // marked) if the list holds fewer than k.  When the k-th value's bin holds
 // at most kRankCap entries, those are ranked directly; otherwise the bins
 // are rebuilt from the top 11 key bits and the radix passes resolve the
-// rest.  hist4 and hist1 are clear on return.  (A
+// rest.  hist_first and hist1 are clear on return.  (A
 // function, not inlined: both maps run the same code.)
 __device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint32_t floor,
                                          uint32_t sft) {
@@ -749,7 +750,7 @@ __device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint
     sh.word[5] = 0u;   // entries gathered (bin, then ties)
   }
   const uint32_t total =
-      find_digit<kSelThreads, kCopies>(B.hist4, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
+      find_digit<kSelThreads, kCopies>(B.hist_first, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
   __syncthreads();
   if (total < k) return false;
   SelState s;
@@ -781,14 +782,14 @@ __device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint
     s.ppre = kPosMask - sh.word[3];  // positions at or below the k-th's
     s.pmask = kPosMask;
   } else {
-    // bins of the top 11 key bits (hist4 is clear: the search read it all)
+    // bins of the top 11 key bits (hist_first is clear: the search read it all)
     const uint32_t copy = static_cast<uint32_t>(lane) & (kCopies - 1);
 #pragma unroll 1
     for (int i = tid; i < n; i += kSelThreads)
-      atomicAdd(&B.hist4[hslot<kCopies>(list[i].x >> 21, copy)], 1u);
+      atomicAdd(&B.hist_first[hslot<kCopies>(list[i].x >> 21, copy)], 1u);
     if (tid == 0) sh.word[5] = 0u;
     __syncthreads();
-    find_digit<kSelThreads, kCopies>(B.hist4, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
+    find_digit<kSelThreads, kCopies>(B.hist_first, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
     __syncthreads();
     s.kpre = sh.word[2] << 21;
     s.kmask = static_cast<uint32_t>(kBins - 1) << 21;
@@ -855,7 +856,7 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
   __syncthreads();
 
   // One map's select: its entries (the target's without the draft's picks)
-  // into the LDS list, their top 11 key bits into hist4, then the select,
+  // into the LDS list, their top 11 key bits into hist_first, then the select,
   // or the streaming fallback.  Called once per map, so that the draft's
   // registers are free during the target's.
   auto run_map = [&](const uint2 (&ev)[kListChunks], uint32_t vmask, bool overflow, int k,
@@ -863,7 +864,7 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
     if (k <= 0) return;
     bool done = false;
     if (!overflow) {
-      for (int i = tid; i < kBins * (kCopies + 1); i += kSelThreads) sh.s.hist4[i] = 0u;
+      for (int i = tid; i < kBins * (kCopies + 1); i += kSelThreads) sh.s.hist_first[i] = 0u;
       const uint32_t copy = static_cast<uint32_t>(lane) & (kCopies - 1);
       bool in_u[kListChunks];
 #pragma unroll
@@ -879,13 +880,21 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
       for (int u = 0; u < kListChunks; ++u) n_mine += in_u[u] ? 1u : 0u;
       uint32_t n_list;
       uint32_t at = block_exclusive_scan<kSelThreads>(n_mine, sh.scan, &n_list);
+      uint32_t n_top = 0;  // entries past the upper estimate: counted per wave
 #pragma unroll
       for (int u = 0; u < kListChunks; ++u) {
         if (!in_u[u]) continue;
         const uint32_t key = order_key(__uint_as_float(ev[u].x));
         sh.list[at++] = make_uint2(key, ev[u].y);
-        atomicAdd(&sh.s.hist4[hslot<kCopies>(rel_bin(key, floor, sft), copy)], 1u);
+        const uint32_t bin = rel_bin(key, floor, sft);
+        if (bin == kBins - 1)
+          ++n_top;
+        else
+          atomicAdd(&sh.s.hist_first[hslot<kCopies>(bin, copy)], 1u);
       }
+      n_top = wave_inclusive_scan(n_top);
+      if (lane == kWave - 1 && n_top != 0u)
+        atomicAdd(&sh.s.hist_first[hslot<kCopies>(kBins - 1, 0)], n_top);
       __syncthreads();
       done = list_select(static_cast<int>(n_list), static_cast<uint32_t>(k), sh, floor, sft);
     }
