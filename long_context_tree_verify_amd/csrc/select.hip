@@ -580,7 +580,12 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(
     uint32_t *counts, uint2 *lists) {
   __shared__ FiltShared sh;
   const int tid = threadIdx.x, lane = tid % kWave;
-  const int bg = blockIdx.x / nch, ch = blockIdx.x % nch;
+  // Chunk-major block order: block i goes to XCD i mod 8, so with a multiple
+  // of 8 rows all chunks of row bg run on the XCD of bg mod 8, where the
+  // floor and list kernels' workgroup for that row runs too (their data
+  // stays in that XCD's L2).
+  const int rows_n = gridDim.x / nch;
+  const int bg = blockIdx.x % rows_n, ch = blockIdx.x / rows_n;
   const int64_t row0 = static_cast<int64_t>(bg) * score_len;
   const float *rows[2] = {draft + row0, target + row0};
   const int c0 = ch * kChunk;
