@@ -6,12 +6,16 @@
 //
 // With 32 query rows every K/V byte feeds only 32 x 128 x 2 multiply-adds,
 // so the kernel is an HBM stream and its job is to keep enough bytes in
-// flight.  One workgroup owns one (split, sequence, KV head); its four waves
-// take every fourth 32-key block of the split, each with its own online
-// softmax, and merge their four results through LDS at the end.  Each wave
-// moves its blocks HBM -> LDS with global_load_lds_dwordx4 into a private
-// two-stage ring and waits only on its own DMA (s_waitcnt vmcnt), so the loop
-// has no workgroup barrier and the four streams drift freely.
+// flight.  One workgroup owns one (split, sequence, KV head); its W waves
+// (two for dense calls, four for sparse ones: Cfg below) take every W-th
+// 32-key block of the split, each with its own online softmax, and merge
+// their results through LDS at the end.  Each wave moves its blocks
+// HBM -> LDS with global_load_lds_dwordx4 into a private two-stage ring and
+// waits only on its own DMA (s_waitcnt vmcnt), so the loop has no workgroup
+// barrier and the streams drift freely.  A dense workgroup takes 66.5 KB of
+// LDS, so two run on each CU (one wave per SIMD): while one starts (query
+// loads, first DMA) or ends (merge, partial stores), the other keeps
+// streaming.
 //
 // Inside a block everything is as in the 256-row kernel (attn_dma.hip): the
 // 1 KB DMA blocks (K: (chunk%4)*256 + (key%16)*16, V: (key%16)*64 +
@@ -49,8 +53,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 
-constexpr int kWaves = 4;                     // waves per workgroup, each on its own blocks
-constexpr int kNT = kWaves * 64;
 constexpr int kRows = 32;                     // grouped query rows (one MFMA column block)
 constexpr int kBK = 32;                       // keys per block
 constexpr int kD = 128;
@@ -62,16 +64,34 @@ constexpr int kWaveLds = kRing * kBlockBytes; // 32 KB
 constexpr int kDmaPerBlock = 2 * kHalfBytes / 1024;  // 16 one-KB DMA instructions
 // Epilogue: each wave's 32 x 128 fp32 accumulator rows (padded) and row stats.
 constexpr int kEpiRow = kD * 4 + 16;
-constexpr int kEpiBytes = kWaves * kRows * kEpiRow + 2 * kWaves * kRows * 4;
-constexpr int kStreamBytes = kWaves * kWaveLds;
 constexpr int kIdxSlot = 64 * 4;               // one block's row indices (64 lanes)
-constexpr int kIdxBytes = kWaves * 2 * kIdxSlot;
-constexpr int kSmemBytes =
-    (kStreamBytes > kEpiBytes ? kStreamBytes : kEpiBytes) + kIdxBytes;
+
+// Workgroup shape.  Dense calls run two waves per workgroup and two
+// workgroups per CU, so one workgroup's start and end hide behind the
+// other's stream (ragged batches run several rounds of workgroups).  Sparse
+// calls (index sets of one length, usually a single round) run four waves
+// and one workgroup per CU: fewer workgroups, epilogues and partials.
+template <int W>
+struct Cfg {
+  static constexpr int kWaves = W;             // waves per workgroup, each on its own blocks
+  static constexpr int kNT = W * 64;
+  static constexpr int kWgPerCu = W == 2 ? 2 : 1;
+  static constexpr int kEpiBytes = W * kRows * kEpiRow + 2 * W * kRows * 4;
+  // the final combination: kEpiTpr threads per row, kEpiFeat features each
+  static constexpr int kEpiTpr = kNT / kRows;
+  static constexpr int kEpiFeat = kD / kEpiTpr;
+  static constexpr int kStreamBytes = W * kWaveLds;
+  static constexpr int kIdxBytes = W * 2 * kIdxSlot;
+  static constexpr int kSmemBytes =
+      (kStreamBytes > kEpiBytes ? kStreamBytes : kEpiBytes) + kIdxBytes;
+  static_assert(kEpiTpr * kEpiFeat == kD && (kEpiTpr & (kEpiTpr - 1)) == 0, "epilogue split");
+  static_assert(kWgPerCu * kSmemBytes <= 160 * 1024, "LDS of the CU's workgroups");
+};
+constexpr int waves_for(bool sparse) { return sparse ? 4 : 2; }
 // sparse over a paged cache: the sequence's block table, after the rest
 constexpr int kTabEntries = 6144;
 constexpr int kTabBytes = kTabEntries * 4;
-static_assert(kSmemBytes + kTabBytes <= 160 * 1024, "LDS of one workgroup");
+static_assert(Cfg<waves_for(true)>::kSmemBytes + kTabBytes <= 160 * 1024, "LDS of one workgroup");
 
 constexpr float kSumLimit = 65536.f;  // as in attn_dma.hip
 
@@ -123,8 +143,105 @@ __device__ __forceinline__ void wait_vm(int n) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ---- slots of a ragged dense batch ---------------------------------------------
+// With equal slot counts the workgroups of a long sequence run longer than
+// those of a short one, and the batch ends on a few long workgroups.  Here
+// sequence b instead gets n_b slots, the largest-remainder share of the
+// n_splits * B slots by its key range len_b, so every slot of the batch has
+// about sum(len) / (n_splits * B) keys; n_b is raised to
+// ceil(len_b / keys_per_split) (no slot longer than the plan's) and to 1, and
+// capped at n_slots, the workspace's slots per (sequence, KV head).  The
+// sum of n_b is at most (n_splits + 1) * B.  Workgroup j takes the j-th
+// (sequence, slot, KV head) triple; a workgroup past
+// the last triple has nothing to do.  The triples run slot by slot (slot s of
+// every sequence that has one, then slot s + 1), as with equal slots.  Every
+// wave computes the same result (B <= 64: lane b holds sequence b).
+struct Job {
+  int b, g, slot, n_b, c;  // c: the sequence's context length (clamped)
+};
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), off, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32), off, kWave);
+    x += static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  }
+  return x;
+}
+
+__device__ bool balanced_job(const Plan &P, int j, int lane, Job *out) {
+  const bool on = lane < P.B;
+  int len = 0, c = 0;
+  if (on) {
+    c = min(max(P.ctx_lens[lane], 0), P.cap - P.N);
+    const int lo = P.has_prefix ? 0 : c;
+    const int hi = P.has_tree ? c + P.N : c;
+    len = hi - lo;
+  }
+  const int64_t J = static_cast<int64_t>(P.n_splits) * P.B;
+  const int64_t T = wave_sum_i64(len);
+  int64_t fl = 0, rem = 0;
+  if (T > 0) {
+    // floor(num / T) through fp64: num < 2^44 and the quotient < 2^15, so
+    // the truncated double quotient is off by at most one
+    const int64_t num = static_cast<int64_t>(len) * J;
+    fl = static_cast<int64_t>(static_cast<double>(num) / static_cast<double>(T));
+    if (fl * T > num)
+      --fl;
+    else if ((fl + 1) * T <= num)
+      ++fl;
+    rem = num - fl * T;
+  }
+  const int64_t D = J - wave_sum_i64(fl);  // slots left for the largest remainders
+  // rank of this lane's remainder among the non-empty sequences (ties by index)
+  const bool elig = on && len > 0;
+  int rank = 0;
+  for (int m = 0; m < P.B; ++m) {
+    const uint32_t rlo = __builtin_amdgcn_readlane(static_cast<uint32_t>(rem), m);
+    const uint32_t rhi =
+        __builtin_amdgcn_readlane(static_cast<uint32_t>(static_cast<uint64_t>(rem) >> 32), m);
+    const int64_t rm = static_cast<int64_t>((static_cast<uint64_t>(rhi) << 32) | rlo);
+    const bool em = __builtin_amdgcn_readlane(static_cast<int>(elig), m) != 0;
+    rank += (em && (rm > rem || (rm == rem && m < lane))) ? 1 : 0;
+  }
+  int n = 0;
+  if (on) {
+    const int64_t lr = fl + ((elig && rank < D) ? 1 : 0);
+    const int base = (len + P.keys_per_split - 1) / P.keys_per_split;
+    n = static_cast<int>(min<int64_t>(max<int64_t>(max<int64_t>(lr, base), 1), P.n_slots));
+  }
+  // slot-major order: slot s of every sequence with n_b > s, KV heads inner
+  int slot = 0, first = 0;
+  uint64_t has;
+  for (;;) {
+    has = __ballot(n > slot);
+    const int cnt = __popcll(has) * P.Hkv;
+    if (cnt == 0) return false;
+    if (j < first + cnt) break;
+    first += cnt;
+    ++slot;
+  }
+  const int r = j - first;
+  const int idx = r / P.Hkv;  // the idx-th sequence (in order) with n_b > slot
+  const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(has >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(has), 0u));
+  const uint64_t pick = __ballot(((has >> lane) & 1) && static_cast<int>(below) == idx);
+  const int b = __ffsll(static_cast<unsigned long long>(pick)) - 1;
+  out->b = b;
+  out->slot = slot;
+  out->g = r - idx * P.Hkv;
+  out->n_b = __builtin_amdgcn_readlane(n, b);
+  out->c = __builtin_amdgcn_readlane(c, b);
+  return true;
+}
+
 template <bool SPARSE, bool SPAGED>
-__global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
+__global__ __launch_bounds__(Cfg<waves_for(SPARSE)>::kNT, Cfg<waves_for(SPARSE)>::kWgPerCu)
+void attn_partial_dma_small(Plan P) {
+  using C = Cfg<waves_for(SPARSE)>;
+  constexpr int kWaves = C::kWaves, kNT = C::kNT, kSmemBytes = C::kSmemBytes;
+  constexpr int kIdxBytes = C::kIdxBytes, kEpiTpr = C::kEpiTpr, kEpiFeat = C::kEpiFeat;
   static_assert(SPARSE || !SPAGED, "paged gathers are sparse");
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes + (SPAGED ? kTabBytes : 0)];
 
@@ -134,29 +251,41 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   const int l32 = lane & 31, hf = lane >> 5;
 
   const int BH = P.B * P.Hkv;
-  const int bg = blockIdx.x % BH;
-  const int slot = blockIdx.x / BH;
-  const int b = bg / P.Hkv, g = bg % P.Hkv;
+  // A ragged dense batch takes balanced slots (the plan then has more slots
+  // than splits); otherwise block j is slot j / BH of (sequence, KV head) j % BH.
+  const bool balanced = !SPARSE && P.n_slots > P.n_splits;
+  int b, g, slot, n_b, c;
+  if (balanced) {
+    Job jb;
+    if (!balanced_job(P, blockIdx.x, lane, &jb)) return;
+    b = jb.b;
+    g = jb.g;
+    slot = jb.slot;
+    n_b = jb.n_b;
+    c = jb.c;
+  } else {
+    slot = blockIdx.x / BH;
+    b = (blockIdx.x % BH) / P.Hkv;
+    g = (blockIdx.x % BH) % P.Hkv;
+    n_b = P.n_splits;
+    c = min(max(P.ctx_lens[b], 0), P.cap - P.N);
+  }
+  const int bg = b * P.Hkv + g;
 
   // ---- key range of this slot (prefix or index set, then draft rows) --------
   // Keys [0, cpos) are the prefix (dense: rows 0..c-1; sparse: rows
   // kv_idx[0..n_sel-1]), keys cpos + j are draft row c + j.
-  const int c = min(max(P.ctx_lens[b], 0), P.cap - P.N);
   const int cpos = SPARSE ? P.n_sel : c;
   const int lo = P.has_prefix ? 0 : cpos;
   const int hi = P.has_tree ? cpos + P.N : cpos;
-  // Each sequence's own key range is cut into the plan's n_splits slots of
-  // equal length (rounded up to whole 32-key blocks, 64 keys for a paged
-  // cache as the plan's slots are), never longer than the plan's slot.  In a
-  // batch of unequal contexts a short sequence then has short slots instead
-  // of empty ones, so every workgroup streams and the last round of
-  // workgroups is not left to a few full-length ones.  With equal contexts
-  // the slots are the plan's.
+  // Each sequence's own key range is cut into its n_b slots of equal length
+  // (rounded up to whole 32-key blocks, 64 keys for a paged cache as the
+  // plan's slots are), never longer than the plan's slot.  With equal
+  // contexts the slots are the plan's.
   const int quantum = (!SPARSE && P.block_table != nullptr) ? 64 : kBK;
   const int len = hi - lo;
   const int kps = min(P.keys_per_split,
-                      max(quantum, ((len + P.n_splits - 1) / P.n_splits + quantum - 1) /
-                                       quantum * quantum));
+                      max(quantum, ((len + n_b - 1) / n_b + quantum - 1) / quantum * quantum));
   const int t_begin = lo + slot * kps;
   const int t_end = min(t_begin + kps, hi);
   const int n_blocks = t_end > t_begin ? (t_end - t_begin + kBK - 1) / kBK : 0;
@@ -167,15 +296,28 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
   const int r = l32;  // this lane's grouped row
   const int64_t prow = (static_cast<int64_t>(slot) * BH + bg) * P.R + r;
 
+  // Balanced slots: the workgroup of a sequence's last slot marks the
+  // workspace slots n_b .. n_slots-1 of its (sequence, KV head) empty.  (Called
+  // where no DMA is in flight: stores count in vmcnt too.)
+  auto mark_unused = [&]() {
+    if (balanced && slot == n_b - 1 && wave == 0 && hf == 0 && r < P.R)
+      for (int s = n_b; s < P.n_slots; ++s) {
+        const int64_t pr = (static_cast<int64_t>(s) * BH + bg) * P.R + r;
+        P.lse_part[pr] = kNegInf;
+        if (P.part_f16) P.o_scale[pr] = 1.f;
+      }
+  };
+
   if (n_blocks == 0) {
     if (wave == 0 && hf == 0 && r < P.R) {
       P.lse_part[prow] = kNegInf;
       if (P.part_f16) P.o_scale[prow] = 1.f;
     }
+    mark_unused();
     return;
   }
 
-  // this wave's blocks: i = wave, wave + 4, ...
+  // this wave's blocks: i = wave, wave + kWaves, ...
   const int my_n = wave < n_blocks ? (n_blocks - wave + kWaves - 1) / kWaves : 0;
 
   const bool paged = !SPARSE && P.block_table != nullptr;
@@ -499,12 +641,13 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     }
   }
 
-  // ---- merge the four waves' results through LDS ---------------------------
+  // ---- merge the waves' results through LDS ---------------------------------
   // Each wave's row statistics (log2-domain reference and sum) and its
   // unnormalised accumulator rows; then every thread combines 16 values of
   // one row: weights 2^(m_w - M) / L with L = sum_w l_w 2^(m_w - M).
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   __syncthreads();  // every wave is done with its ring
+  mark_unused();
   float *stat_m = reinterpret_cast<float *>(smem + kWaves * kRows * kEpiRow);
   float *stat_l = stat_m + kWaves * kRows;
   if (hf == 0) {
@@ -525,8 +668,8 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     }
   __syncthreads();
 
-  // thread -> (row, 16 features): 8 threads per row, rows 0..31
-  const int row = tid >> 3, f0 = (tid & 7) * 16;
+  // thread -> (row, kEpiFeat features): kEpiTpr threads per row, rows 0..31
+  const int row = tid / kEpiTpr, f0 = (tid % kEpiTpr) * kEpiFeat;
   float mw[kWaves], lw[kWaves];
   float M = kNegInf;
 #pragma unroll
@@ -542,15 +685,15 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
     L += lw[w] * sc[w];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float o16[16];
+  float o16[kEpiFeat];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) o16[e] = 0.f;
+  for (int e = 0; e < kEpiFeat; ++e) o16[e] = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const float wt = sc[w] * inv;
     const float *src = reinterpret_cast<const float *>(smem + (w * kRows + row) * kEpiRow) + f0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o16[e] = fmaf(wt, src[e], o16[e]);
+    for (int e = 0; e < kEpiFeat; ++e) o16[e] = fmaf(wt, src[e], o16[e]);
   }
   if (!P.part_f16) {
     // fp32 partial rows (HSV_FLAG_F32_PARTIALS)
@@ -558,34 +701,33 @@ __global__ __launch_bounds__(kNT, 1) void attn_partial_dma_small(Plan P) {
       const int64_t orow = (static_cast<int64_t>(slot) * BH + bg) * P.R + row;
       float *dst = P.o_part + orow * kD + f0;
 #pragma unroll
-      for (int e = 0; e < 16; e += 4)
+      for (int e = 0; e < kEpiFeat; e += 4)
         *reinterpret_cast<float4 *>(dst + e) = make_float4(o16[e], o16[e + 1], o16[e + 2],
                                                            o16[e + 3]);
-      if ((tid & 7) == 0) P.lse_part[orow] = L > 0.f ? (M + fast_log2(L)) * kLn2 : kNegInf;
+      if (tid % kEpiTpr == 0) P.lse_part[orow] = L > 0.f ? (M + fast_log2(L)) * kLn2 : kNegInf;
     }
     return;
   }
   // scaled fp16: the row's largest |value| in [0.5, 1), scale to o_scale
   float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o16[e]));
+  for (int e = 0; e < kEpiFeat; ++e) amax = fmaxf(amax, fabsf(o16[e]));
 #pragma unroll
-  for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  for (int off = 1; off < kEpiTpr; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
   int ex = 0;
   if (amax > 0.f && amax < __builtin_huge_valf()) (void)frexpf(amax, &ex);
   const float mul = ldexpf(1.f, -ex);
   if (row < P.R) {
     const int64_t orow = (static_cast<int64_t>(slot) * BH + bg) * P.R + row;
-    halfx8 h0, h1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      h0[e] = static_cast<_Float16>(o16[e] * mul);
-      h1[e] = static_cast<_Float16>(o16[8 + e] * mul);
-    }
     _Float16 *dst = reinterpret_cast<_Float16 *>(P.o_part) + orow * kD + f0;
-    *reinterpret_cast<halfx8 *>(dst) = h0;
-    *reinterpret_cast<halfx8 *>(dst + 8) = h1;
-    if ((tid & 7) == 0) {
+#pragma unroll
+    for (int e0 = 0; e0 < kEpiFeat; e0 += 8) {
+      halfx8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(o16[e0 + e] * mul);
+      *reinterpret_cast<halfx8 *>(dst + e0) = h;
+    }
+    if (tid % kEpiTpr == 0) {
       P.lse_part[orow] = L > 0.f ? (M + fast_log2(L)) * kLn2 : kNegInf;
       P.o_scale[orow] = ldexpf(1.f, ex);
     }
@@ -600,21 +742,27 @@ bool dma_small_supports(const Plan &p) {
          (p.n_sel == 0 || static_cast<int64_t>(p.cap) * kRowBytes < (int64_t{1} << 32));
 }
 
-int dma_small_tile_keys() { return kWaves * kBK; }
+// the planner's slot unit: a slot is split further while longer than 64 of these
+int dma_small_tile_keys() { return 4 * kBK; }
+int dma_small_wgs_per_cu(bool sparse) {
+  return sparse ? Cfg<waves_for(true)>::kWgPerCu : Cfg<waves_for(false)>::kWgPerCu;
+}
 
 int dma_small_table_entries() { return kTabEntries; }
 
 hipError_t launch_attn_partials_dma_small(const Plan &p, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(p.n_slots) * p.B * p.Hkv;
+  // balanced slots (n_slots > n_splits): at most (n_splits + 1) * B triples per KV head
+  const int64_t grid_slots = p.n_slots > p.n_splits ? p.n_splits + 1 : p.n_slots;
+  const int64_t blocks = grid_slots * p.B * p.Hkv;
   if (p.n_sel > 0 && p.block_table)
     hipLaunchKernelGGL((attn_partial_dma_small<true, true>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kNT), 0, s, p);
+                       dim3(Cfg<waves_for(true)>::kNT), 0, s, p);
   else if (p.n_sel > 0)
     hipLaunchKernelGGL((attn_partial_dma_small<true, false>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kNT), 0, s, p);
+                       dim3(Cfg<waves_for(true)>::kNT), 0, s, p);
   else
     hipLaunchKernelGGL((attn_partial_dma_small<false, false>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kNT), 0, s, p);
+                       dim3(Cfg<waves_for(false)>::kNT), 0, s, p);
   return hipGetLastError();
 }
 

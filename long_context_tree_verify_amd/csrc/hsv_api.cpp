@@ -136,10 +136,10 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
       (p->kernel != kKernDmaSmall || d->kv_capacity / d->block_size > dma_small_table_entries()))
     return HSV_ERR_UNSUPPORTED;
   if (p->unified) {
-    // One key range per (b, kv head): prefix (or index set) then draft rows.  One workgroup
-    // per CU: as many splits as fit in one round of the CUs (splits of a
-    // multiple of 32 keys), more only when the batch is ragged and a split
-    // would exceed 64 tiles.
+    // One key range per (b, kv head): prefix (or index set) then draft rows.  As many
+    // splits as fit in one round of the CUs (one workgroup per CU, two for
+    // dense calls on the small-group kernel; splits of a multiple of 32 keys), more only
+    // when the batch is ragged and a split would exceed 64 tiles.
     const int64_t keys = (with_prefix ? (sparse ? d->n_sel : d->max_ctx) : 0) +
                          (with_tree ? d->n_draft : 0);
     const int64_t units = static_cast<int64_t>(p->B) * p->Hkv * p->row_chunks;
@@ -147,7 +147,14 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
     if (d->num_splits > 0) {
       target = d->num_splits;
     } else {
-      target = std::max<int64_t>(1, kPlanCUs / units);
+      // the small-group kernel runs several workgroups per CU
+      const int64_t slots =
+          p->kernel == kKernDmaSmall ? kPlanCUs * dma_small_wgs_per_cu(sparse) : kPlanCUs;
+      target = std::max<int64_t>(1, slots / units);
+      // A dense batch there takes two rounds of workgroups: its slots are
+      // shared out by key range (see below), and the second round evens out
+      // what the rounding of that share leaves unequal.
+      if (p->kernel == kKernDmaSmall && !sparse && p->B > 1) target *= 2;
       if (p->B > 1)
         while (ceil_div(keys, target * tile) > 64 && target * 2 <= kMaxSplits) target *= 2;
     }
@@ -167,6 +174,13 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
     p->n_splits = keys > 0 ? static_cast<int32_t>(ceil_div(keys, kps)) : 0;
     p->tree_slot = -1;
     p->n_slots = p->n_splits;
+    // A dense batch of several sequences on the small-group kernel: the
+    // kernel shares n_splits * B slots among the sequences in proportion to
+    // their key ranges, so one sequence may take more than n_splits; the
+    // workspace holds 2 * n_splits slots per (sequence, KV head), and a
+    // longer share is capped there.
+    if (p->kernel == kKernDmaSmall && !sparse && p->B > 1 && p->B <= 64 && p->n_splits > 0)
+      p->n_slots = 2 * p->n_splits;
     p->n_parts = p->n_slots * p->kgroups;
     p->part_f16 = (d->flags & HSV_FLAG_F32_PARTIALS) ? 0 : 1;
     *ws_bytes = workspace_bytes(*p);

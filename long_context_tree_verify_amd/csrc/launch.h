@@ -31,6 +31,7 @@ hipError_t launch_attn_partials_dma_small(const Plan &p, hipStream_t s);
 // The per-wave DMA variant for small groups: dense bf16, head_dim 128, <= 32 rows.
 bool dma_small_supports(const Plan &p);
 int dma_small_tile_keys();
+int dma_small_wgs_per_cu(bool sparse);
 int dma_small_table_entries();  // block-table columns a paged sparse call may have
 
 // Prefix splits and the tree part -> o_part / lse_part.

@@ -6,6 +6,8 @@ oracle computes one by one.  Mask, index and gather handling must be
 bit-exact; O within 1e-2 max-abs and the LSE within 1e-3 relative.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -111,6 +113,48 @@ def test_dma_path_edges(hsv, gpu, over, wl):
         o, lse = run_hip(hsv, inp, dev, num_splits=splits)
         assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"splits={splits}")
 
+
+
+# Dense batches of several sequences on the small-group kernel share
+# n_splits * B slots among the sequences by key range: a long sequence among
+# short or empty ones asks for more than twice the split count and is capped
+# there, tiny ones still take one slot, empty ones (no keys without the tree)
+# take one that writes nothing; 64 sequences is the largest batch shared
+# that way and 65 falls back to equal slots.
+BALANCED_CASES = [
+    ("skewed", 12, (3000, 0, 5, 1, 0, 31, 2, 0, 0, 7, 3, 0)),
+    ("one long", 6, (2900, 40, 40, 40, 40, 40)),
+    ("b64", 64, None),   # contexts drawn from [0, 600]
+    ("b65", 65, None),
+]
+
+
+@pytest.mark.parametrize("label,batch,ctx", BALANCED_CASES)
+def test_small_kernel_balanced_slots(hsv, gpu, label, batch, ctx):
+    if ctx is None:
+        inp = cached_inputs("chain_b16", (("ctx", (0, 600)), ("batch", batch)))
+    else:
+        # every sequence drawn at the longest context, then cut to its own
+        # length, with the rows past c + N poisoned again
+        inp = cached_inputs("chain_b16", (("ctx", (max(ctx), max(ctx))), ("batch", batch)))
+        c = np.array(ctx, dtype=np.int32)
+        nan = np.uint16(0x7FC0) if inp.k.dtype == np.uint16 else np.float32(np.nan)
+        k, v = inp.k.copy(), inp.v.copy()
+        for b in range(batch):
+            k[b, :, c[b] + inp.wl.n_draft:] = nan
+            v[b, :, c[b] + inp.wl.n_draft:] = nan
+        inp = dataclasses.replace(inp, ctx_lens=c, k=k, v=v)
+    log(f"balanced {label} B={batch} ctx={inp.ctx_lens.tolist()[:12]}")
+    dev = device_inputs(inp, gpu)
+    o_ref, l_ref = _oracle_all(inp)
+    for splits in (0, 3, 64):
+        o, lse = run_hip(hsv, inp, dev, num_splits=splits)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"{label} splits={splits}")
+    for flag, part in ((hsv.HSV_FLAG_NO_TREE, oracle.PART_PREFIX),
+                       (hsv.HSV_FLAG_NO_PREFIX, oracle.PART_TREE)):
+        o, lse = run_hip(hsv, inp, dev, flags=flag)
+        o_ref, l_ref = _oracle_all(inp, parts=part)
+        assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"{label} flag={flag}")
 
 # Keys scored far above everything before them (32x the row, so the score
 # jumps by many log2 units), placed mid-range, at the last row of a 32-key
