@@ -284,8 +284,9 @@ hsv_status hsv_accept_path(void *k_cache, void *v_cache, int32_t *ctx_lens,
  * Requires n_sink + n_recent <= n_sel, n_draft_top >= 0 and
  * score_len <= 524288; the chosen set is unique (no randomness).
  * `workspace` (device, 256-byte aligned, at least
- * hsv_select_workspace_bytes) holds the candidate lists between the two
- * launches; its contents on entry do not matter. */
+ * hsv_select_workspace_bytes) holds the per-row floors and the candidate
+ * lists between the call's three launches; its contents on entry do not
+ * matter. */
 hsv_status hsv_select_kv_idx(const float *draft_score, const float *target_score,
                              int32_t score_len, const int32_t *ctx_lens, int32_t batch,
                              int32_t n_kv_heads, int32_t n_sel, int32_t n_sink,
@@ -294,8 +295,8 @@ hsv_status hsv_select_kv_idx(const float *draft_score, const float *target_score
                              hipStream_t stream);
 
 /* Bytes of workspace hsv_select_kv_idx needs for these sizes (per (b, KV
- * head) and 8192-position chunk of the score rows, two candidate lists of
- * 1024 (key, position) slots and their counts).  HSV_ERR_SHAPE /
+ * head) four words of floors, and per 8192-position chunk of its score rows
+ * two candidate lists of 1024 (key, position) slots and their counts).  HSV_ERR_SHAPE /
  * HSV_ERR_UNSUPPORTED for sizes the call would reject. */
 hsv_status hsv_select_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t score_len,
                                       size_t *bytes);
