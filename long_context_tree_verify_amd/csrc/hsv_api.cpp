@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstring>
 
 #include "hsv.h"
 #include "launch.h"
@@ -473,7 +474,12 @@ hsv_status hsv_lse_merge(const float *o_parts, const float *lse_parts, int32_t n
 }
 
 const char *hsv_status_string(hsv_status s) {
-  switch (s) {
+  // A C caller may pass any int: read its bits instead of loading the enum
+  // (a value outside the enumeration's range is not a valid hsv_status).
+  static_assert(sizeof(hsv_status) == sizeof(int), "hsv_status is passed as an int");
+  int code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case HSV_OK: return "HSV_OK: success";
     case HSV_ERR_NULL: return "HSV_ERR_NULL: a required pointer is NULL";
     case HSV_ERR_SHAPE: return "HSV_ERR_SHAPE: sizes out of range or inconsistent";
