@@ -1,0 +1,81 @@
+"""A seeded random sweep over the shapes the verify calls accept, each case
+against the fp64 oracle on every output row.
+
+The hand-picked parity cases cover each kernel at its edges; this sweep
+draws combinations nobody picked -- batch, draft nodes, query and KV heads,
+head dim, input and output dtype, dense or sparse, tree shape, ragged
+contexts, split count, partial format -- so that a planner decision or a
+work mapping that only fails on some pairing is still met.  Every draw is
+fixed by its case number; sizes are kept where the oracle takes about a
+second.  (Random trees branch at most 4 ways, so a depth of at least 4 holds
+256 nodes.)
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from util import assert_parity, device_inputs, log, run_hip
+
+N_CASES = 120
+ROW_KEY_BUDGET = 2e7   # (output rows) x (keys per row) the oracle is given
+
+
+@pytest.fixture(scope="module")
+def hsv(gpu):
+    import long_context_tree_verify_amd as m
+    return m
+
+
+def draw_case(k: int):
+    rng = np.random.default_rng(1000 + k)
+    pick = lambda xs: xs[int(rng.integers(len(xs)))]
+    dtype = "bf16" if rng.random() < 0.75 else "f32"
+    D = pick([64, 128])
+    Hkv = pick([1, 2, 4, 8])
+    G = pick([1, 2, 4, 8])
+    N = pick([1, 2, 5, 8, 16, 31, 64, 65, 100, 256])
+    B = pick([1, 2, 3, 5, 8, 17])
+    tree = pick(["uniform", "tree", "chain"])
+    hi = pick([0, 1, 33, 100, 700, 3000])
+    lo = int(rng.integers(0, hi + 1)) if rng.random() < 0.7 else hi
+    n_sel = 0
+    if dtype == "bf16" and rng.random() < 0.3:
+        n_sel = pick([1, 7, 64, 300])
+        hi = max(hi, n_sel + 10)
+        lo = max(lo, n_sel)
+    # keep the oracle's work bounded
+    while B * N * G * Hkv * (hi + N) > ROW_KEY_BUDGET and (B > 1 or hi > n_sel + 10):
+        if B > 1:
+            B = max(1, B // 2)
+        else:
+            hi = max(n_sel + 10, hi // 2)
+            lo = min(lo, hi)
+    over = dict(batch=B, n_draft=N, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=D,
+                ctx=(lo, hi), dtype=dtype, tree=tree,
+                max_depth=int(rng.integers(4, max(5, N) + 1)) if tree == "tree" else 0)
+    if n_sel:
+        n_sink = min(4, n_sel // 4)
+        over.update(n_sel=n_sel, n_sink=n_sink, n_recent=min(n_sel - n_sink, n_sel // 2))
+    run = dict(num_splits=pick([0, 0, 1, 3, 64]),
+               out_bf16=bool(rng.random() < 0.25),
+               f32_partials=bool(rng.random() < 0.2))
+    return over, run, int(1000 + k)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("k", range(N_CASES))
+def test_random_shape(hsv, gpu, k):
+    import torch
+    over, run, seed = draw_case(k)
+    base = "tree32k" if over["dtype"] == "bf16" else "tiny_tree"
+    inp = synth.make_inputs(base, seed=seed, **over)
+    log(f"random case {k}: {over} {run} ctx={inp.ctx_lens.tolist()[:8]}")
+    dev = device_inputs(inp, gpu)
+    flags = hsv.HSV_FLAG_F32_PARTIALS if run["f32_partials"] else 0
+    out = torch.bfloat16 if run["out_bf16"] else torch.float32
+    o, lse = run_hip(hsv, inp, dev, num_splits=run["num_splits"], flags=flags, out_dtype=out)
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                                      kv_idx=inp.kv_idx, bf16=inp.is_bf16)
+    assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"random case {k}")
