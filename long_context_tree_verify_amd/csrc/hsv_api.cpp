@@ -163,12 +163,13 @@ hsv_status make_plan(const hsv_verify_desc *d, bool sparse, Plan *p, size_t *ws_
     // pool block) spanning at most 33 pool blocks (one table entry per
     // lane).  Paged sparse rows are translated one by one: no constraint.
     int64_t quantum = 32;
+    target = std::max<int64_t>(1, std::min<int64_t>(target, kMaxSplits));
     if (paged && !sparse) {
       quantum = 64;
-      target = std::max<int64_t>(target, ceil_div(keys, 32 * static_cast<int64_t>(d->block_size)));
-      if (target > kMaxSplits) return HSV_ERR_UNSUPPORTED;
+      const int64_t need = ceil_div(keys, 32 * static_cast<int64_t>(d->block_size));
+      if (need > kMaxSplits) return HSV_ERR_UNSUPPORTED;
+      target = std::max<int64_t>(target, need);
     }
-    target = std::max<int64_t>(1, std::min<int64_t>(target, kMaxSplits));
     const int64_t kps =
         std::max<int64_t>(quantum, ceil_div(ceil_div(keys, target), quantum) * quantum);
     p->keys_per_split = static_cast<int32_t>(kps);

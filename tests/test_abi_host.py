@@ -177,6 +177,10 @@ def test_product_package_does_not_reach_the_oracle():
     (dict(block_size=64, n_draft=16, n_q_heads=32), 3),          # 64 rows: MFMA kernel
     (dict(block_size=64, head_dim=64), 3),                       # D 64
     (dict(block_size=64, max_ctx=600000, kv_capacity=600064), 3),  # > 256 splits of 2048 keys
+    # one (sequence, KV head) on the small-group kernel: the split target for
+    # all of the CUs' workgroups exceeds the split limit and is clamped to it
+    (dict(block_size=1024, batch=1, n_q_heads=1, n_kv_heads=1, n_draft=5, max_ctx=100,
+          kv_capacity=1024), 0),
 ])
 def test_paged_descriptors(hsv, kw, code):
     if kw.get("block_size") and "kv_capacity" not in kw:
