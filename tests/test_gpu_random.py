@@ -8,7 +8,8 @@ contexts, split count, partial format -- so that a planner decision or a
 work mapping that only fails on some pairing is still met.  Every draw is
 fixed by its case number; sizes are kept where the oracle takes about a
 second.  (Random trees branch at most 4 ways, so a depth of at least 4 holds
-256 nodes.)
+256 nodes.)  Dense cases whose workspace fits the library's scratch also run
+hsv_verify_attn_noalloc, which must give identical results.
 """
 
 import numpy as np
@@ -79,3 +80,18 @@ def test_random_shape(hsv, gpu, k):
     o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
                                       kv_idx=inp.kv_idx, bf16=inp.is_bf16)
     assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"random case {k}")
+    # the entry point that allocates nothing runs the same plan on the
+    # library's scratch: identical results where the workspace fits it
+    if inp.kv_idx is None:
+        d = hsv.make_desc(batch=inp.wl.batch, n_draft=inp.wl.n_draft, n_q_heads=inp.wl.n_q_heads,
+                          n_kv_heads=inp.wl.n_kv_heads, head_dim=inp.wl.head_dim,
+                          kv_capacity=inp.k.shape[2], max_ctx=int(inp.ctx_lens.max()),
+                          in_dtype=hsv.HSV_BF16 if inp.is_bf16 else hsv.HSV_F32,
+                          out_dtype=hsv.HSV_BF16 if run["out_bf16"] else hsv.HSV_F32,
+                          num_splits=run["num_splits"], flags=flags)
+        if hsv.hsv_verify_workspace_bytes(d) <= hsv.HSV_NOALLOC_SCRATCH_BYTES:
+            o2, l2 = torch.empty_like(o), torch.empty_like(lse)
+            hsv.hsv_verify_attn_noalloc(dev["q"], dev["k"], dev["v"], dev["ctx"], dev["parent"],
+                                        max_ctx=int(inp.ctx_lens.max()), o=o2, lse=l2,
+                                        num_splits=run["num_splits"], flags=flags)
+            assert torch.equal(o2, o) and torch.equal(l2, lse), f"case {k}: no-alloc differs"
