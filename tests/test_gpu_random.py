@@ -62,7 +62,21 @@ def draw_case(k: int):
     run = dict(num_splits=pick([0, 0, 1, 3, 64]),
                out_bf16=bool(rng.random() < 0.25),
                f32_partials=bool(rng.random() < 0.2))
+    # an explicit visibility mask instead of the parents in a quarter of the
+    # cases: random bits (rows may see nothing of the draft block) or the
+    # block-parallel masks of FlexDraft
+    u = rng.random()
+    run["mask"] = None if u < 0.75 else ("random" if u < 0.875 and N <= 64 else "block")
+    run["mask_arg"] = float(rng.uniform(0.05, 0.9)) if run["mask"] == "random" else int(
+        rng.integers(1, N + 1))
     return over, run, int(1000 + k)
+
+
+def make_mask(run, B, N, seed):
+    if run["mask"] == "random":
+        return synth.random_masks(np.random.default_rng(seed), B, N, run["mask_arg"])
+    m = synth.block_masks(N, run["mask_arg"])
+    return np.broadcast_to(m, (B,) + m.shape).copy()
 
 
 @pytest.mark.gpu
@@ -76,9 +90,16 @@ def test_random_shape(hsv, gpu, k):
     dev = device_inputs(inp, gpu)
     flags = hsv.HSV_FLAG_F32_PARTIALS if run["f32_partials"] else 0
     out = torch.bfloat16 if run["out_bf16"] else torch.float32
-    o, lse = run_hip(hsv, inp, dev, num_splits=run["num_splits"], flags=flags, out_dtype=out)
-    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
-                                      kv_idx=inp.kv_idx, bf16=inp.is_bf16)
+    anc = anc_t = None
+    if run["mask"]:
+        anc = make_mask(run, inp.wl.batch, inp.wl.n_draft, seed)
+        anc_t = torch.from_numpy(anc.view(np.int64)).to(gpu)
+        dev = dict(dev, parent=None)
+    o, lse = run_hip(hsv, inp, dev, num_splits=run["num_splits"], flags=flags, out_dtype=out,
+                     anc=anc_t)
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens,
+                                      parent=None if anc is not None else inp.parent,
+                                      anc_mask=anc, kv_idx=inp.kv_idx, bf16=inp.is_bf16)
     assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"random case {k}")
     # the entry point that allocates nothing runs the same plan on the
     # library's scratch: identical results where the workspace fits it
@@ -92,6 +113,6 @@ def test_random_shape(hsv, gpu, k):
         if hsv.hsv_verify_workspace_bytes(d) <= hsv.HSV_NOALLOC_SCRATCH_BYTES:
             o2, l2 = torch.empty_like(o), torch.empty_like(lse)
             hsv.hsv_verify_attn_noalloc(dev["q"], dev["k"], dev["v"], dev["ctx"], dev["parent"],
-                                        max_ctx=int(inp.ctx_lens.max()), o=o2, lse=l2,
+                                        anc_t, max_ctx=int(inp.ctx_lens.max()), o=o2, lse=l2,
                                         num_splits=run["num_splits"], flags=flags)
             assert torch.equal(o2, o) and torch.equal(l2, lse), f"case {k}: no-alloc differs"
