@@ -10,6 +10,10 @@
  * The library keeps no mutable global state, so concurrent calls on different
  * streams with different workspaces are safe -- except hsv_verify_attn_noalloc,
  * whose scratch is one library-owned array per GPU (see there).
+ * Except under HSV_FLAG_VALIDATE, a call enqueues kernel launches only (no
+ * memset, copy or synchronisation), so it may be captured into a HIP graph
+ * and replayed; a validating call synchronises `stream` and cannot be
+ * captured.
  *
  * What is computed.  LongSpec ("Long-Context Lossless Speculative Decoding
  * with Efficient Drafting and Verification"), section 2.C "Hybrid Tree
