@@ -357,12 +357,21 @@ __global__ __launch_bounds__(C::NT, 1) void attn_partial_mfma(Plan P) {
         }
       }
 
-      // mask: keys past the slot's end, and the tree's non-ancestors.  The
-      // lane's 16 keys are kb0 + 4*hf + (8j + r); bit 8j + r of `keep` says
-      // whether that key is visible.
-      if (tree || kb0 + 32 > nv) {
+      // Sparse slots: a key whose index lies outside [0, c) (an out-of-range
+      // entry or the -1 tail) was loaded as a zero row and takes no part.
+      // The tile's row table (ring slot j % 3, not refilled before the next
+      // tile) holds -1 for it; bit i of valid_w is key kb0 + i.
+      uint32_t valid_w = ~0u;
+      if (gather)
+        valid_w = static_cast<uint32_t>(__ballot(srows[SPARSE ? j % 3 : 0][SPARSE ? kb0 + l32 : 0] >= 0));
+
+      // mask: keys past the slot's end, invalid sparse keys and the tree's
+      // non-ancestors.  The lane's 16 keys are kb0 + 4*hf + (8j + r); bit
+      // 8j + r of `keep` says whether that key is visible.
+      if (tree || kb0 + 32 > nv || valid_w != ~0u) {
         const int room = nv - kb0 - 4 * hf;  // visible keys start at bit 0
         uint32_t lim = room <= 0 ? 0u : room >= 32 ? ~0u : ((1u << room) - 1u);
+        lim &= valid_w >> (4 * hf);
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
           uint32_t keep = lim;

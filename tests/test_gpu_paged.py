@@ -205,3 +205,17 @@ def test_sparse_paged_full_size_sparse64k(hsv, gpu):
     o_err, l_err = assert_all_rows(o, lse, inp, "paged sparse64k bs=64", o_ref, l_ref)
     log(f"paged sparse64k bs=64: all rows max|dO| = {o_err:.3e}, max rel dLSE = {l_err:.3e}")
     torch.cuda.empty_cache()
+
+
+def test_sparse_paged_out_of_range_indices_are_masked(hsv, gpu):
+    """Index entries outside [0, c) in a paged sparse call take no part and
+    are never turned into a pool address: the result is that of the set
+    without them (the pool's spare blocks and unselected rows hold NaN)."""
+    from test_gpu_parity import _garbage_indices
+    inp = cached_inputs("sparse64k", SPARSE_CASES[0][0], poison=True)
+    kp, vp, table = _paged(inp, SPARSE_CASES[0][1], 151)
+    bad, clean = _garbage_indices(inp.kv_idx, inp.ctx_lens, inp.k.shape[2], 152)
+    o, lse = _run_sparse(hsv, gpu, inp, kp, vp, table, bad)
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                                      kv_idx=clean, bf16=True)
+    assert_parity(o, lse, o_ref, l_ref, "paged sparse, garbage indices")

@@ -483,3 +483,58 @@ def test_f32_partials_small(hsv, gpu, wl):
     run_hip(hsv, inp, dev, flags=F | hsv.HSV_FLAG_PHASE_PARTIALS, o=o2, lse=l2, workspace=ws)
     run_hip(hsv, inp, dev, flags=F | hsv.HSV_FLAG_PHASE_MERGE, o=o2, lse=l2, workspace=ws)
     assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+# Index-set entries outside [0, c) -- negative, at or just past the context,
+# past the cache, the int32 extremes -- take no part and are never read (the
+# kernels turn them into a masked in-set row before forming an address):
+# the result is that of the set without them.  Runs the small-group kernel
+# (bf16, D 128, 20 grouped rows), the register-staged MFMA kernel (D 64) and
+# the fp32 kernel; unselected rows hold NaN.
+def _garbage_indices(kv_idx, ctx, cap, seed):
+    """kv_idx with about 15 % of its valid entries replaced by out-of-range
+    values, and the same set with those entries removed (-1 tail)."""
+    rng = np.random.default_rng(seed)
+    bad = kv_idx.copy()
+    clean = np.full_like(kv_idx, -1)
+    B, H, n = kv_idx.shape
+    for b in range(B):
+        junk = np.array([-3, ctx[b], ctx[b] + 1, cap + 100, 1 << 30, -(1 << 31)], np.int64)
+        for g in range(H):
+            row = bad[b, g]
+            hit = (row >= 0) & (rng.random(n) < 0.15)
+            row[hit] = junk[rng.integers(0, len(junk), int(hit.sum()))].astype(np.int32)
+            keep = row[(row >= 0) & (row < ctx[b])]
+            clean[b, g, :keep.size] = keep
+    return bad, clean
+
+
+@pytest.mark.parametrize("over", [(), (("head_dim", 64),), (("dtype", "f32"),)])
+def test_sparse_out_of_range_indices_are_masked(hsv, gpu, over):
+    import torch
+    inp = cached_inputs("sparse64k", SPARSE_CASES[1] + tuple(over), poison=True)
+    bad, clean = _garbage_indices(inp.kv_idx, inp.ctx_lens, inp.k.shape[2], 150)
+    dev = dict(device_inputs(inp, gpu), kv_idx=torch.from_numpy(bad).to(gpu))
+    o, lse = run_hip(hsv, inp, dev)
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                                      kv_idx=clean, bf16=inp.is_bf16)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"garbage indices {over}")
+
+
+# Valid index sets ending in -1 slots (the selection writes them when the
+# context is shorter than the set) on every sparse kernel: the small-group
+# kernel, the register-staged MFMA kernel (D 64; 64 grouped rows) and the
+# fp32 kernel.  Sequence 0 keeps its first 30 entries, sequence 1 none.
+@pytest.mark.parametrize("over", [(), (("head_dim", 64),), (("n_draft", 16),),
+                                  (("dtype", "f32"),)])
+def test_sparse_minus_one_tails_every_kernel(hsv, gpu, over):
+    import torch
+    inp = cached_inputs("sparse64k", SPARSE_CASES[1] + tuple(over), poison=True)
+    idx = inp.kv_idx.copy()
+    idx[0, :, 30:] = -1
+    idx[1] = -1
+    dev = dict(device_inputs(inp, gpu), kv_idx=torch.from_numpy(idx).to(gpu))
+    o, lse = run_hip(hsv, inp, dev)
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                                      kv_idx=idx, bf16=inp.is_bf16)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"-1 tails {over}")
