@@ -69,7 +69,23 @@ def draw_case(k: int):
     run["mask"] = None if u < 0.75 else ("random" if u < 0.875 and N <= 64 else "block")
     run["mask_arg"] = float(rng.uniform(0.05, 0.9)) if run["mask"] == "random" else int(
         rng.integers(1, N + 1))
+    # index sets cut short by -1 slots; one part alone; a score scale of the
+    # caller's; the partials and the merge as two calls on one workspace
+    run["tail_seed"] = int(rng.integers(1 << 30)) if n_sel and rng.random() < 0.3 else None
+    run["part"] = pick([None] * 8 + ["prefix", "tree"])
+    run["scale"] = float(np.float32(rng.uniform(0.02, 0.3))) if rng.random() < 0.2 else 0.0
+    run["phase_split"] = bool(rng.random() < 0.2)
     return over, run, int(1000 + k)
+
+
+def cut_tails(kv_idx, seed):
+    """kv_idx with the sets of some sequences cut short by -1 slots."""
+    rng = np.random.default_rng(seed)
+    idx = kv_idx.copy()
+    for b in range(idx.shape[0]):
+        if rng.random() < 0.6:
+            idx[b, :, int(rng.integers(0, idx.shape[2] + 1)):] = -1
+    return idx
 
 
 def make_mask(run, B, N, seed):
@@ -89,21 +105,49 @@ def test_random_shape(hsv, gpu, k):
     log(f"random case {k}: {over} {run} ctx={inp.ctx_lens.tolist()[:8]}")
     dev = device_inputs(inp, gpu)
     flags = hsv.HSV_FLAG_F32_PARTIALS if run["f32_partials"] else 0
+    parts = oracle.PART_BOTH
+    if run["part"] == "prefix":
+        flags |= hsv.HSV_FLAG_NO_TREE
+        parts = oracle.PART_PREFIX
+    elif run["part"] == "tree":
+        flags |= hsv.HSV_FLAG_NO_PREFIX
+        parts = oracle.PART_TREE
     out = torch.bfloat16 if run["out_bf16"] else torch.float32
     anc = anc_t = None
     if run["mask"]:
         anc = make_mask(run, inp.wl.batch, inp.wl.n_draft, seed)
         anc_t = torch.from_numpy(anc.view(np.int64)).to(gpu)
         dev = dict(dev, parent=None)
+    kv_idx = inp.kv_idx
+    if run["tail_seed"] is not None:
+        kv_idx = cut_tails(kv_idx, run["tail_seed"])
+        dev = dict(dev, kv_idx=torch.from_numpy(kv_idx).to(gpu))
     o, lse = run_hip(hsv, inp, dev, num_splits=run["num_splits"], flags=flags, out_dtype=out,
-                     anc=anc_t)
+                     anc=anc_t, scale=run["scale"])
     o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens,
                                       parent=None if anc is not None else inp.parent,
-                                      anc_mask=anc, kv_idx=inp.kv_idx, bf16=inp.is_bf16)
+                                      anc_mask=anc, kv_idx=kv_idx, bf16=inp.is_bf16,
+                                      scale=run["scale"] or None, parts=parts)
     assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"random case {k}")
+    if run["phase_split"]:
+        # the partials, then the merge, as two calls on one workspace
+        d = hsv.make_desc(batch=inp.wl.batch, n_draft=inp.wl.n_draft, n_q_heads=inp.wl.n_q_heads,
+                          n_kv_heads=inp.wl.n_kv_heads, head_dim=inp.wl.head_dim,
+                          kv_capacity=inp.k.shape[2], max_ctx=int(inp.ctx_lens.max()),
+                          n_sel=0 if kv_idx is None else kv_idx.shape[2],
+                          in_dtype=hsv.HSV_BF16 if inp.is_bf16 else hsv.HSV_F32,
+                          out_dtype=hsv.HSV_BF16 if run["out_bf16"] else hsv.HSV_F32,
+                          num_splits=run["num_splits"], flags=flags, scale=run["scale"])
+        ws = torch.empty(max(256, hsv.hsv_verify_workspace_bytes(d)), dtype=torch.uint8,
+                         device=gpu)
+        o3, l3 = torch.empty_like(o), torch.empty_like(lse)
+        for phase in (hsv.HSV_FLAG_PHASE_PARTIALS, hsv.HSV_FLAG_PHASE_MERGE):
+            run_hip(hsv, inp, dev, num_splits=run["num_splits"], flags=flags | phase,
+                    out_dtype=out, anc=anc_t, scale=run["scale"], o=o3, lse=l3, workspace=ws)
+        assert torch.equal(o3, o) and torch.equal(l3, lse), f"case {k}: two-phase call differs"
     # the entry point that allocates nothing runs the same plan on the
     # library's scratch: identical results where the workspace fits it
-    if inp.kv_idx is None:
+    if inp.kv_idx is None and run["scale"] == 0.0:
         d = hsv.make_desc(batch=inp.wl.batch, n_draft=inp.wl.n_draft, n_q_heads=inp.wl.n_q_heads,
                           n_kv_heads=inp.wl.n_kv_heads, head_dim=inp.wl.head_dim,
                           kv_capacity=inp.k.shape[2], max_ctx=int(inp.ctx_lens.max()),
