@@ -160,3 +160,34 @@ def test_random_shape(hsv, gpu, k):
                                         anc_t, max_ctx=int(inp.ctx_lens.max()), o=o2, lse=l2,
                                         num_splits=run["num_splits"], flags=flags)
             assert torch.equal(o2, o) and torch.equal(l2, lse), f"case {k}: no-alloc differs"
+
+
+# Large grids, beyond the sweep's sizes: many sequences (past the 64 that
+# share slots by key range), many KV heads (MHA with 64 heads), and query
+# groups of 512 and 1024 rows (several 256-row chunks per KV head, on the
+# XCD-aware chunk order and off it), with short contexts for the oracle.
+LARGE_CASES = [
+    dict(batch=128, n_draft=8, n_q_heads=4, n_kv_heads=1, head_dim=128, ctx=(20, 200), dtype="bf16", tree="chain"),
+    dict(batch=70, n_draft=4, n_q_heads=16, n_kv_heads=8, head_dim=128, ctx=(0, 300), dtype="bf16", tree="uniform"),
+    dict(batch=3, n_draft=16, n_q_heads=64, n_kv_heads=64, head_dim=128, ctx=(100, 400), dtype="bf16", tree="tree", max_depth=6),
+    dict(batch=2, n_draft=64, n_q_heads=64, n_kv_heads=8, head_dim=128, ctx=(300, 500), dtype="bf16", tree="tree", max_depth=8),
+    dict(batch=1, n_draft=128, n_q_heads=64, n_kv_heads=8, head_dim=128, ctx=(700, 700), dtype="bf16", tree="tree", max_depth=10),
+    dict(batch=5, n_draft=128, n_q_heads=24, n_kv_heads=3, head_dim=128, ctx=(50, 400), dtype="bf16", tree="uniform"),
+    dict(batch=40, n_draft=8, n_q_heads=32, n_kv_heads=32, head_dim=64, ctx=(0, 150), dtype="f32", tree="chain"),
+    dict(batch=96, n_draft=8, n_q_heads=32, n_kv_heads=8, head_dim=128, ctx=(100, 200), dtype="bf16",
+         tree="chain", n_sel=64, n_sink=4, n_recent=16),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(len(LARGE_CASES)))
+def test_large_grid(hsv, gpu, case):
+    over = LARGE_CASES[case]
+    base = "tree32k" if over["dtype"] == "bf16" else "tiny_tree"
+    inp = synth.make_inputs(base, seed=9000 + case, **over)
+    log(f"large grid case {case}: {over}")
+    dev = device_inputs(inp, gpu)
+    o, lse = run_hip(hsv, inp, dev)
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
+                                      kv_idx=inp.kv_idx, bf16=inp.is_bf16)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, f"large grid case {case}")
