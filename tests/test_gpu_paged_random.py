@@ -8,8 +8,9 @@ Draws stay within the shapes the paged calls accept (bf16, head dim 128,
 the 256-row kernel's more than 128 grouped rows or the small-group kernel's
 at most 32; sparse only on the latter): batch, draft nodes, query and KV
 heads, block size 64 to 1024, ragged contexts including 0, index-set size
-and split count.  Pool blocks are in a seeded random order and the spare
-ones hold NaN.  Every draw is fixed by its case number.
+split count and, for a third of the dense calls, an explicit visibility
+mask (random bits or block-parallel) instead of the parents.  Pool blocks
+are in a seeded random order and the spare ones hold NaN.  Every draw is fixed by its case number.
 """
 
 import numpy as np
@@ -56,18 +57,36 @@ def draw_case(k: int):
     while B * N * G * Hkv * (hi + N) > 2e7 and B > 1:
         B = over["batch"] = max(1, B // 2)
     over["ctx"] = (lo, hi)
+    # an explicit visibility mask instead of the parents in a third of the
+    # cases (dense calls): random bits up to 64 nodes, else block-parallel
+    u = rng.random()
+    mask = None if sparse or u < 0.67 else ("random" if N <= 64 and u < 0.85 else "block")
+    over["_mask"] = (mask, int(rng.integers(1, N + 1)))
     return over, bs, pick([0, 1, 5]), 3000 + k
 
 
 @pytest.mark.parametrize("k", range(N_CASES))
 def test_random_paged(hsv, gpu, k):
+    import torch
     over, bs, splits, seed = draw_case(k)
+    mask, arg = over.pop("_mask")
     inp = synth.make_inputs("tree32k", seed=seed, **over)
     kp, vp, table = _paged(inp, bs, seed)
     log(f"paged case {k}: {over} bs={bs} splits={splits} ctx={inp.ctx_lens.tolist()}")
-    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens, parent=inp.parent,
-                                      kv_idx=inp.kv_idx, bf16=True)
-    if inp.kv_idx is None:
+    anc = None
+    if mask == "random":
+        anc = synth.random_masks(np.random.default_rng(seed), inp.wl.batch, inp.wl.n_draft,
+                                 0.1 + 0.8 * (arg % 8) / 8)
+    elif mask == "block":
+        m = synth.block_masks(inp.wl.n_draft, arg)
+        anc = np.broadcast_to(m, (inp.wl.batch,) + m.shape).copy()
+    o_ref, l_ref = oracle.verify_attn(inp.q, inp.k, inp.v, inp.ctx_lens,
+                                      parent=None if anc is not None else inp.parent,
+                                      anc_mask=anc, kv_idx=inp.kv_idx, bf16=True)
+    if inp.kv_idx is None and anc is not None:
+        o, lse = _run(hsv, gpu, inp, kp, vp, table, num_splits=splits, parent=None,
+                      anc=torch.from_numpy(anc.view(np.int64)).to(gpu))
+    elif inp.kv_idx is None:
         o, lse = _run(hsv, gpu, inp, kp, vp, table, num_splits=splits)
     else:
         o, lse = _run_sparse(hsv, gpu, inp, kp, vp, table, inp.kv_idx, num_splits=splits)
