@@ -55,6 +55,11 @@ hsv_status hsv_verify_attn_noalloc(const hsv_verify_desc *d, const void *q, cons
   const hsv_status st = hsv_verify_workspace_bytes(d, &need);
   if (st != HSV_OK) return st;
   if (need > kScratchBytes) return HSV_ERR_WORKSPACE;
+  // Argument errors come before any runtime call, as in hsv_verify_attn:
+  // the tree part needs exactly one of parent and anc_mask.
+  if (!q || !k_cache || !v_cache || !ctx_lens || !o || !lse) return HSV_ERR_NULL;
+  if (!(d->flags & HSV_FLAG_NO_TREE) && ((parent == nullptr) == (anc_mask == nullptr)))
+    return HSV_ERR_NULL;
   int device = -1;
   if (hipStreamGetDevice(stream, &device) != hipSuccess) return HSV_ERR_HIP;
   void *ws = scratch_on(device);
