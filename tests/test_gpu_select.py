@@ -146,6 +146,20 @@ def test_rows_past_64k(hsv, gpu):
            n_recent=0, n_draft_top=1790)
 
 
+def test_candidates_starting_past_the_first_chunk(hsv, gpu):
+    # sinks that cover one or more whole 8192-position chunks, so the first
+    # candidate (whose chunk publishes the row's floors for the list step)
+    # lies in a later chunk, on a chunk boundary or inside one; contexts
+    # below the sink count leave rows with no candidates at all
+    rng = np.random.Generator(np.random.PCG64(517))
+    L = 65536
+    ctx = np.array([65536, 40000, 9000, 16384, 20000], np.int32)
+    draft, target = synth.importance_maps(rng, ctx, 2, L)
+    for n_sink in (9000, 16384, 8191):
+        _check(hsv, gpu, draft, target, ctx, f"n_sink {n_sink}", n_sel=n_sink + 4096,
+               n_sink=n_sink, n_recent=512, n_draft_top=1790)
+
+
 def test_rejects_bad_arguments(hsv, gpu):
     import torch
     d = torch.zeros((1, 1, 16), dtype=torch.float32, device=gpu)
