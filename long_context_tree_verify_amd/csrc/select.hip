@@ -28,12 +28,13 @@
 //     with one float compare per score; the scores that pass (raw bits and
 //     position) are appended to the chunk's own slots in the workspace.
 //  3. select_lists (one 1024-thread workgroup per row): every list slot of
-//     both maps is loaded at once.  Per map the listed keys (the target's
-//     without the draft's picks) move to an LDS list while the histogram of
-//     their top 11 bits is built; that gives the first digit, the next
-//     passes take key bits 10..20 and 0..9 (skipped when every entry left
-//     shares them), and the few entries left sharing the k-th key are
-//     ranked by position directly.  A list answers the question whenever at
+//     both maps is loaded at once and stays in registers.  One pass counts
+//     both maps' listed keys into floor-relative histograms (the draft's
+//     picks leave the target's once they are known); the first digit then
+//     names the bin of the k-th value, whose few entries are ranked
+//     directly, or the radix passes take key bits 10..20 and 0..9 (skipped
+//     when every entry left shares them) and the few entries left sharing
+//     the k-th key are ranked by position.  A list answers the question whenever at
 //     least k listed candidates remain: then the k-th best is at or above
 //     the floor, and every candidate at or above the floor was listed.
 //     Otherwise (or if a list overflowed, or candidates lie past the first
@@ -58,7 +59,6 @@ constexpr int kChunk = 8192;          // positions per filter workgroup
 constexpr int kQuads = kChunk / (4 * kFiltThreads);  // 16-byte loads per thread and map
 constexpr int kChunkCap = 1024;       // list slots per (chunk, map)
 constexpr int kListChunks = 8;        // rows of up to 8 chunks take the list path
-constexpr int kListCap = kListChunks * kChunkCap;
 constexpr int kListMax = kListChunks * kChunk;  // 65536 positions with list slots
 constexpr int kBitsMax = kListMax + kChunk;     // rows the list path takes (a 64k context plus
                                                 // its draft rows); entries past kListMax go to
@@ -302,7 +302,8 @@ __device__ __forceinline__ bool in_prefix(const uint2 v, const SelState &s) {
 }
 
 // Passes 2..5 of the select (key bits 10..20 and 0..9, then inverted
-// position bits 8..18 and 0..7) over entries[0, n) by the whole workgroup;
+// position bits 8..18 and 0..7) over the entries the workgroup's threads hold
+// (entry u of a thread present when bit u of `held` is set);
 // done as soon as every entry of the current bin is taken.  The low-key-bit
 // pass is skipped when every entry left after pass 2 shares those bits
 // (seen during pass 2).  Once the key is resolved, up to kTieCap entries
@@ -311,8 +312,9 @@ __device__ __forceinline__ bool in_prefix(const uint2 v, const SelState &s) {
 // clear; it is clear again on return.  sh_word[0] / [1] / [5] must hold
 // 0 / ~0 / 0 (or / and of low key bits, tie count); sh_word[2..4] and [6]
 // carry results between threads; tie holds kTieCap positions.
-__device__ void late_passes(const uint2 *entries, int n, uint32_t *hist, uint32_t *scan,
-                            uint32_t *sh_word, uint32_t *tie, SelState &s) {
+__device__ __forceinline__ void late_passes(const uint2 (&ent)[kListChunks], uint32_t held,
+                                            uint32_t *hist, uint32_t *scan, uint32_t *sh_word,
+                                            uint32_t *tie, SelState &s) {
   const int tid = threadIdx.x, lane = tid % kWave;
   uint32_t lo_or = 0u, lo_and = ~0u;
 #pragma unroll 1
@@ -323,10 +325,10 @@ __device__ void late_passes(const uint2 *entries, int n, uint32_t *hist, uint32_
     const uint32_t dmask = pass == 2 ? 1023u : pass == 4 ? 255u : 2047u;
     if (pass == 3 && s.in_bin <= static_cast<uint32_t>(kTieCap)) {
       // the entries with the k-th key, by position: gather, rank, cut
-#pragma unroll 1
-      for (int i = tid; i < n; i += kSelThreads) {
-        const uint2 v = entries[i];
-        if (v.x == s.kpre) tie[atomicAdd(&sh_word[5], 1u)] = v.y;
+#pragma unroll
+      for (int u = 0; u < kListChunks; ++u) {
+        const uint2 v = ent[u];
+        if (((held >> u) & 1u) && v.x == s.kpre) tie[atomicAdd(&sh_word[5], 1u)] = v.y;
       }
       __syncthreads();
       if (tid < static_cast<int>(s.in_bin)) {
@@ -360,10 +362,10 @@ __device__ void late_passes(const uint2 *entries, int n, uint32_t *hist, uint32_
         continue;
       }
     }
-#pragma unroll 1
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint2 v = entries[i];
-      if (in_prefix(v, s)) {
+#pragma unroll
+    for (int u = 0; u < kListChunks; ++u) {
+      const uint2 v = ent[u];
+      if (((held >> u) & 1u) && in_prefix(v, s)) {
         const uint32_t inv = kPosMask - v.y;
         atomicAdd(&hist[((on_pos ? inv : v.x) >> shift) & dmask], 1u);
         if (pass == 1) {
@@ -716,7 +718,8 @@ struct alignas(16) SelBufs {
 };
 struct alignas(16) ListShared {
   uint32_t bits[kWords];            // chosen positions of the row
-  uint2 list[kListCap];             // one map's listed entries (key, position)
+  uint32_t hist_t[kBins * kCopies]; // the target map's first histogram
+  uint2 stash[kListChunks][kSelThreads];  // the target's entries while the draft's run
   union {
     SelBufs s;
     StreamShared stream;            // the fallback
@@ -737,25 +740,25 @@ __device__ __forceinline__ bool value_above(const uint2 a, const uint2 b) {
   return a.x > b.x || (a.x == b.x && a.y < b.y);
 }
 
-// The exact k best (k >= 1) of list[0, n) into `bits`, with hist_first holding
-// the entries' floor-relative bin counts (kCopies copies); false (nothing
-// marked) if the list holds fewer than k.  When the k-th value's bin holds
-// at most kRankCap entries, those are ranked directly; otherwise the bins
-// are rebuilt from the top 11 key bits and the radix passes resolve the
-// rest.  hist_first and hist1 are clear on return.  (A
-// function, not inlined: both maps run the same code.)
-__device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint32_t floor,
-                                         uint32_t sft) {
+// The exact k best (k >= 1) of the listed entries into `bits`: entry u of a
+// thread (key, position) is listed when bit u of `held` is set, and `first`
+// holds the listed entries' floor-relative bin counts; false (nothing
+// marked) if fewer than k are listed.  When the k-th value's bin holds at
+// most kRankCap entries, those are ranked directly; otherwise the bins are
+// rebuilt from the top 11 key bits and the radix passes resolve the rest.
+// `first`, hist_first and hist1 are clear on return.
+__device__ __forceinline__ bool list_select(const uint2 (&ent)[kListChunks], uint32_t held,
+                                            uint32_t k, ListShared &sh, uint32_t *first,
+                                            uint32_t floor, uint32_t sft) {
   const int tid = threadIdx.x, lane = tid % kWave;
   SelBufs &B = sh.s;
-  const uint2 *list = sh.list;
   if (tid == 0) {
     sh.word[0] = 0u;   // or of low key bits
     sh.word[1] = ~0u;  // and
     sh.word[5] = 0u;   // entries gathered (bin, then ties)
   }
   const uint32_t total =
-      find_digit<kSelThreads, kCopies>(B.hist_first, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
+      find_digit<kSelThreads, kCopies>(first, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
   __syncthreads();
   if (total < k) return false;
   SelState s;
@@ -765,10 +768,11 @@ __device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint
   __syncthreads();  // sh.word[2..4] are rewritten below
   if (s.in_bin <= static_cast<uint32_t>(kRankCap)) {
     // the bin's entries, ranked by value: the need-th is the k-th overall
-#pragma unroll 1
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint2 v = list[i];
-      if (rel_bin(v.x, floor, sft) == d1) B.cand[atomicAdd(&sh.word[5], 1u)] = v;
+#pragma unroll
+    for (int u = 0; u < kListChunks; ++u) {
+      const uint2 v = ent[u];
+      if (((held >> u) & 1u) && rel_bin(v.x, floor, sft) == d1)
+        B.cand[atomicAdd(&sh.word[5], 1u)] = v;
     }
     __syncthreads();
     if (tid < static_cast<int>(s.in_bin)) {
@@ -787,11 +791,12 @@ __device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint
     s.ppre = kPosMask - sh.word[3];  // positions at or below the k-th's
     s.pmask = kPosMask;
   } else {
-    // bins of the top 11 key bits (hist_first is clear: the search read it all)
+    // bins of the top 11 key bits (hist_first is clear: it was never used,
+    // or it was `first` and the search read it all)
     const uint32_t copy = static_cast<uint32_t>(lane) & (kCopies - 1);
-#pragma unroll 1
-    for (int i = tid; i < n; i += kSelThreads)
-      atomicAdd(&B.hist_first[hslot<kCopies>(list[i].x >> 21, copy)], 1u);
+#pragma unroll
+    for (int u = 0; u < kListChunks; ++u)
+      if ((held >> u) & 1u) atomicAdd(&B.hist_first[hslot<kCopies>(ent[u].x >> 21, copy)], 1u);
     if (tid == 0) sh.word[5] = 0u;
     __syncthreads();
     find_digit<kSelThreads, kCopies>(B.hist_first, k, sh.scan, &sh.word[2], &sh.word[3], &sh.word[4]);
@@ -802,15 +807,16 @@ __device__ __noinline__ bool list_select(int n, uint32_t k, ListShared &sh, uint
     s.need = sh.word[3];
     s.in_bin = sh.word[4];
     __syncthreads();  // sh.word[2..4] are rewritten below
-    late_passes(list, n, B.hist1, sh.scan, sh.word, B.tie, s);
+    late_passes(ent, held, B.hist1, sh.scan, sh.word, B.tie, s);
   }
   // every value at or above the k-th: above its bin in the resolved key
   // bits, or inside it and at or above it in the resolved position bits
-#pragma unroll 1
-  for (int i = tid; i < n; i += kSelThreads) {
-    const uint2 v = list[i];
+#pragma unroll
+  for (int u = 0; u < kListChunks; ++u) {
+    const uint2 v = ent[u];
     const uint32_t kx = v.x & s.kmask;
-    if (kx > s.kpre || (kx == s.kpre && ((kPosMask - v.y) & s.pmask) >= s.ppre))
+    if (((held >> u) & 1u) &&
+        (kx > s.kpre || (kx == s.kpre && ((kPosMask - v.y) & s.pmask) >= s.ppre)))
       atomicOr(&sh.bits[v.y >> 5], 1u << (v.y & 31));
   }
   __syncthreads();
@@ -825,17 +831,23 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
   const int tid = threadIdx.x, lane = tid % kWave;
   const int bg = blockIdx.x;
 
-  // Every list slot this thread holds (slot tid of each chunk of both maps:
-  // raw score bits and position) is loaded before anything waits; chunks
-  // past nch repeat the last one and are dropped below.
+  // Every list slot this thread holds (raw score bits and position) is
+  // loaded before anything waits: slot (tid + 128 u) mod 1024 of chunk u of
+  // both maps.  A chunk's list fills its first slots, so the rotation gives
+  // every thread a share of the entries rather than all eight slots to the
+  // first few hundred threads.  Chunks past nch repeat the last one and are
+  // dropped below.
+  constexpr int kTurn = kChunkCap / kListChunks;
+  static_assert(kSelThreads == kChunkCap, "one slot of each chunk per thread");
   uint2 e[2][kListChunks];
   {
-    const uint2 *src = lists + static_cast<int64_t>(bg) * nch * 2 * kChunkCap + tid;
+    const uint2 *src = lists + static_cast<int64_t>(bg) * nch * 2 * kChunkCap;
 #pragma unroll
     for (int u = 0; u < kListChunks; ++u)
 #pragma unroll
       for (int map = 0; map < 2; ++map)
-        e[map][u] = src[(static_cast<int64_t>(min(u, nch - 1)) * 2 + map) * kChunkCap];
+        e[map][u] = src[(static_cast<int64_t>(min(u, nch - 1)) * 2 + map) * kChunkCap +
+                        ((tid + kTurn * u) & (kChunkCap - 1))];
   }
   const Budget bd = budget(ctx_lens[bg / hkv], score_len, n_sel, n_sink, n_recent, n_draft_top);
   const int words = (bd.c + 31) / 32;
@@ -852,63 +864,92 @@ __global__ __launch_bounds__(kSelThreads) void select_lists_kernel(
     for (int map = 0; map < 2; ++map) {
       const uint32_t n = u < nch ? counts[(static_cast<int64_t>(bg) * nch + u) * 2 + map] : 0u;
       over[map] = over[map] || n > static_cast<uint32_t>(kChunkCap);
-      if (static_cast<uint32_t>(tid) < n) valid[map] |= 1u << u;
+      if (static_cast<uint32_t>((tid + kTurn * u) & (kChunkCap - 1)) < n) valid[map] |= 1u << u;
     }
   for (int u = kListChunks; u < nch; ++u)
 #pragma unroll
     for (int map = 0; map < 2; ++map)
       over[map] = over[map] || counts[(static_cast<int64_t>(bg) * nch + u) * 2 + map] != 0u;
+  for (int i = tid; i < kBins * (kCopies + 1); i += kSelThreads) sh.s.hist_first[i] = 0u;
+  for (int i = tid; i < kBins * kCopies; i += kSelThreads) sh.hist_t[i] = 0u;
   __syncthreads();
 
-  // One map's select: its entries (the target's without the draft's picks)
-  // into the LDS list, their top 11 key bits into hist_first, then the select,
-  // or the streaming fallback.  Called once per map, so that the draft's
-  // registers are free during the target's.
-  auto run_map = [&](const uint2 (&ev)[kListChunks], uint32_t vmask, bool overflow, int k,
-                     const float *row, bool target_map, uint32_t floor, uint32_t sft) {
-    if (k <= 0) return;
-    bool done = false;
-    if (!overflow) {
-      for (int i = tid; i < kBins * (kCopies + 1); i += kSelThreads) sh.s.hist_first[i] = 0u;
-      const uint32_t copy = static_cast<uint32_t>(lane) & (kCopies - 1);
-      bool in_u[kListChunks];
+  // Both maps' entries stay in registers.  One pass turns their scores into
+  // keys and counts them into the maps' first histograms (floor-relative
+  // bins); the target's still counts the entries the draft will pick, which
+  // leave it once they are known.
+  uint32_t fl[2], sf[2];
+  bool use[2];
+  const uint32_t copy = static_cast<uint32_t>(lane) & (kCopies - 1);
 #pragma unroll
-      for (int u = 0; u < kListChunks; ++u) {
-        const bool ok = (vmask >> u) & 1u;
-        const uint32_t py = ok ? ev[u].y : 0u;  // an empty slot's position is not read
-        in_u[u] = ok && !(target_map && ((sh.bits[py >> 5] >> (py & 31)) & 1u));
-      }
-      // each thread's entries go to consecutive list slots (a prefix sum
-      // over the workgroup; the scan's barriers also order the clearing)
-      uint32_t n_mine = 0;
+  for (int map = 0; map < 2; ++map) {
+    fl[map] = floors[4 * bg + 2 * map];
+    sf[map] = floors[4 * bg + 2 * map + 1];
+    use[map] = (map == 0 ? bd.m : bd.rest) > 0 && !over[map];
+    if (!use[map]) continue;
+    uint32_t *first = map == 0 ? sh.s.hist_first : sh.hist_t;
+    uint32_t n_top = 0;  // entries past the upper estimate: counted per wave
 #pragma unroll
-      for (int u = 0; u < kListChunks; ++u) n_mine += in_u[u] ? 1u : 0u;
-      uint32_t n_list;
-      uint32_t at = block_exclusive_scan<kSelThreads>(n_mine, sh.scan, &n_list);
-      uint32_t n_top = 0;  // entries past the upper estimate: counted per wave
-#pragma unroll
-      for (int u = 0; u < kListChunks; ++u) {
-        if (!in_u[u]) continue;
-        const uint32_t key = order_key(__uint_as_float(ev[u].x));
-        sh.list[at++] = make_uint2(key, ev[u].y);
-        const uint32_t bin = rel_bin(key, floor, sft);
-        if (bin == kBins - 1)
-          ++n_top;
-        else
-          atomicAdd(&sh.s.hist_first[hslot<kCopies>(bin, copy)], 1u);
-      }
-      n_top = wave_inclusive_scan(n_top);
-      if (lane == kWave - 1 && n_top != 0u)
-        atomicAdd(&sh.s.hist_first[hslot<kCopies>(kBins - 1, 0)], n_top);
-      __syncthreads();
-      done = list_select(static_cast<int>(n_list), static_cast<uint32_t>(k), sh, floor, sft);
+    for (int u = 0; u < kListChunks; ++u) {
+      if (!((valid[map] >> u) & 1u)) continue;
+      const uint32_t key = order_key(__uint_as_float(e[map][u].x));
+      e[map][u].x = key;
+      const uint32_t bin = rel_bin(key, fl[map], sf[map]);
+      if (bin == kBins - 1)
+        ++n_top;
+      else
+        atomicAdd(&first[hslot<kCopies>(bin, copy)], 1u);
     }
-    if (!done) select_best(row, bd.lo, bd.hi, static_cast<uint32_t>(k), sh.bits, sh.stream);
-  };
+    n_top = wave_inclusive_scan(n_top);
+    if (lane == kWave - 1 && n_top != 0u) atomicAdd(&first[hslot<kCopies>(kBins - 1, 0)], n_top);
+  }
+  // the target's entries wait in this thread's LDS slots, so that one set
+  // of registers holds the current map's
+  if (use[1]) {
+#pragma unroll
+    for (int u = 0; u < kListChunks; ++u) sh.stash[u][tid] = e[1][u];
+  }
+  __syncthreads();
+
+  // The draft's m best, then the target's rest best among the candidates
+  // the draft left: each over its list, or by the streaming fallback.  One
+  // code path serves both maps.
   const int64_t row0 = static_cast<int64_t>(bg) * score_len;
-  run_map(e[0], valid[0], over[0], bd.m, draft + row0, false, floors[4 * bg], floors[4 * bg + 1]);
-  run_map(e[1], valid[1], over[1], bd.rest, target + row0, true, floors[4 * bg + 2],
-          floors[4 * bg + 3]);
+  uint2 ent[kListChunks];
+#pragma unroll
+  for (int u = 0; u < kListChunks; ++u) ent[u] = e[0][u];
+#pragma unroll 1
+  for (int map = 0; map < 2; ++map) {
+    const int k = map == 0 ? bd.m : bd.rest;
+    if (k <= 0) continue;
+    uint32_t held = map == 0 ? valid[0] : valid[1];
+    const bool use_list = map == 0 ? use[0] : use[1];
+    if (map == 1) {
+      if (use_list) {
+#pragma unroll
+        for (int u = 0; u < kListChunks; ++u) {
+          ent[u] = sh.stash[u][tid];
+          const bool ok = (held >> u) & 1u;
+          const uint32_t py = ok ? ent[u].y : 0u;  // an empty slot's position is not read
+          if (ok && ((sh.bits[py >> 5] >> (py & 31)) & 1u)) {
+            held &= ~(1u << u);
+            atomicSub(&sh.hist_t[hslot<kCopies>(rel_bin(ent[u].x, fl[1], sf[1]), copy)], 1u);
+          }
+        }
+      }
+      // the draft's streaming fallback shares these buffers
+      for (int i = tid; i < kBins * (kCopies + 1); i += kSelThreads) sh.s.hist_first[i] = 0u;
+      __syncthreads();
+    }
+    bool done = false;
+    if (use_list)
+      done = list_select(ent, held, static_cast<uint32_t>(k), sh,
+                         map == 0 ? sh.s.hist_first : sh.hist_t, map == 0 ? fl[0] : fl[1],
+                         map == 0 ? sf[0] : sf[1]);
+    if (!done)
+      select_best((map == 0 ? draft : target) + row0, bd.lo, bd.hi, static_cast<uint32_t>(k),
+                  sh.bits, sh.stream);
+  }
   write_set(sh.bits, bd, n_sel, kv_idx + static_cast<int64_t>(bg) * n_sel, sh.scan);
 }
 
