@@ -18,7 +18,7 @@ from test_gpu_accept import _cache, _check_accept, _trees
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 60
+N_CASES = 200
 
 
 @pytest.fixture(scope="module")

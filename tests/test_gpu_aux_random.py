@@ -14,7 +14,7 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 30
+N_CASES = 100
 
 
 @pytest.fixture(scope="module")

@@ -23,7 +23,7 @@ from util import assert_parity, log
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 50
+N_CASES = 150
 
 
 @pytest.fixture(scope="module")

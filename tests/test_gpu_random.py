@@ -19,7 +19,7 @@ import oracle
 import synth
 from util import assert_parity, device_inputs, log, run_hip
 
-N_CASES = 120
+N_CASES = 400
 ROW_KEY_BUDGET = 2e7   # (output rows) x (keys per row) the oracle is given
 
 

@@ -20,7 +20,7 @@ from util import log
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 150
+N_CASES = 400
 LENGTHS = [1, 7, 100, 2000, 8192, 8193, 20000, 65536, 65544, 73728, 73729, 100000]
 
 
