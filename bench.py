@@ -803,9 +803,10 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "hsv runs on one GPU (no collectives); --gpus must be 1",
                           "n_gpus": args.gpus}))
-        log("bench.py: only --gpus 1 is supported (single-GPU build; no collectives)")
+        log("bench.py: only --gpus 1 is supported: the library runs on one GPU and has no "
+            "collectives")
         return 2
     if args.steps < 1 or args.warmup < 0:
         log("bench.py: --steps must be >= 1 and --warmup >= 0")
