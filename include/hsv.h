@@ -84,7 +84,7 @@ typedef enum hsv_status {
   HSV_OK = 0,
   HSV_ERR_NULL = 1,         /* a required pointer is NULL                        */
   HSV_ERR_SHAPE = 2,        /* sizes out of range or inconsistent                */
-  HSV_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement       */
+  HSV_ERR_UNSUPPORTED = 3,  /* valid request the library does not implement     */
   HSV_ERR_WORKSPACE = 4,    /* workspace missing, too small or misaligned        */
   HSV_ERR_DEVICE_CHECK = 5, /* HSV_FLAG_VALIDATE found bad device-side data      */
   HSV_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed        */

@@ -484,7 +484,7 @@ const char *hsv_status_string(hsv_status s) {
     case HSV_OK: return "HSV_OK: success";
     case HSV_ERR_NULL: return "HSV_ERR_NULL: a required pointer is NULL";
     case HSV_ERR_SHAPE: return "HSV_ERR_SHAPE: sizes out of range or inconsistent";
-    case HSV_ERR_UNSUPPORTED: return "HSV_ERR_UNSUPPORTED: request not implemented by this build";
+    case HSV_ERR_UNSUPPORTED: return "HSV_ERR_UNSUPPORTED: a valid request the library does not implement";
     case HSV_ERR_WORKSPACE: return "HSV_ERR_WORKSPACE: workspace missing, too small or misaligned";
     case HSV_ERR_DEVICE_CHECK: return "HSV_ERR_DEVICE_CHECK: device-side input check failed";
     case HSV_ERR_HIP: return "HSV_ERR_HIP: HIP runtime or launch failure";
