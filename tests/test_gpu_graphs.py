@@ -2,8 +2,9 @@
 eager work and synchronisations in between: every replay must give the eager
 result bit for bit (the benchmark times graph replays).  Covers the
 two-launch selection (workspace lists between the launches), the paged
-attention, the 256-node tree (masks built in the workspace) and the
-accepted-path update (two launches; the lengths restored before each)."""
+attention, the 256-node tree (masks built in the workspace), the
+accepted-path update (two launches; the lengths restored before each) and
+the entry point without a workspace (its scratch is the library's own)."""
 
 import numpy as np
 import pytest
@@ -140,3 +141,22 @@ def test_accept_graph(hsv, gpu):
         _ = torch.ones(1024, device=gpu).sum()
         torch.cuda.synchronize()
     log("  accepted-path update: 3 replays identical")
+
+
+def test_noalloc_graph(hsv, gpu):
+    # the call callers under graph capture use: its scratch is a library-owned
+    # per-GPU array, looked up by the first (eager) call
+    import torch
+    inp = cached_inputs("tree32k", (("ctx", (4000, 4000)),))
+    dev = device_inputs(inp, gpu)
+    mc = int(inp.ctx_lens.max())
+    o_ref, l_ref = hsv.hsv_verify_attn(dev["q"], dev["k"], dev["v"], dev["ctx"], dev["parent"],
+                                       max_ctx=mc)
+    o, lse = torch.empty_like(o_ref), torch.empty_like(l_ref)
+    call = lambda: hsv.hsv_verify_attn_noalloc(dev["q"], dev["k"], dev["v"], dev["ctx"],
+                                               dev["parent"], max_ctx=mc, o=o, lse=lse)
+    call()
+    torch.cuda.synchronize()
+    for i, (o_g, l_g) in enumerate(_replay(gpu, call, [o, lse])):
+        assert torch.equal(o_g, o_ref) and torch.equal(l_g, l_ref), f"replay {i} differs"
+    log("  no-alloc call in a graph: every replay identical to the eager workspace call")
